@@ -1,0 +1,147 @@
+"""Python binding of libfa.so, the gfx950 exact-attention library.
+
+Argument marshalling only: every step of the attention path runs in the HIP
+kernels behind the C ABI declared in include/fa.h.  PyTorch supplies device
+memory and the current stream.  There is no fallback: if the library is not
+built, or the tensors are not on a ROCm device, the calls raise.
+
+Functions mirror the C entry points:
+  fa_fwd(q, k, v, o, lse, scale, causal)                       -> None
+  fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale, causal, ws)   -> None
+  fa_bwd_workspace_size(B, H, N, d, causal)                    -> int
+  fa_strerror(status)                                          -> str
+plus allocating conveniences forward(...) and backward(...).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first so libfa.so binds to the HIP runtime torch already holds
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+HEAD_DIM = 128
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_WORKSPACE = 3
+FA_ERR_HIP = 4
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"libfa status {status}: {fa_strerror(status)}")
+        self.status = status
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libfa.so (built in-tree by exact_io_aware_10_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_10_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_fwd.restype = i
+        lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
+        lib.fa_bwd_workspace_size.restype = sz
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+        lib.fa_bwd.restype = i
+        lib.fa_strerror.argtypes = [i]
+        lib.fa_strerror.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def fa_strerror(status: int) -> str:
+    return load_library().fa_strerror(int(status)).decode()
+
+
+def fa_bwd_workspace_size(B: int, H: int, N: int, d: int = HEAD_DIM, causal: bool = False) -> int:
+    return int(load_library().fa_bwd_workspace_size(B, H, N, d, int(bool(causal))))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_tensor(name, t, dtype, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _shape(q):
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    return tuple(q.shape)
+
+
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
+    B, H, N, d = _shape(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_tensor(name, t, torch.bfloat16, (B, H, N, d))
+    _check_tensor("lse", lse, torch.float32, (B, H, N))
+    st = load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                               float(scale), int(bool(causal)), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st)
+
+
+def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, workspace,
+           stream=None) -> None:
+    B, H, N, d = _shape(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dO", do), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        _check_tensor(name, t, torch.bfloat16, (B, H, N, d))
+    _check_tensor("lse", lse, torch.float32, (B, H, N))
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                               _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
+                               _ptr(workspace), nbytes, _stream(stream))
+    if st != FA_OK:
+        raise FAError(st)
+
+
+def forward(q, k, v, scale: float, causal: bool, stream=None):
+    """Allocate O and LSE with torch and run fa_fwd.  Returns (o, lse)."""
+    B, H, N, d = _shape(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale, causal, stream)
+    return o, lse
+
+
+def workspace_for(B, H, N, causal, device):
+    n = max(fa_bwd_workspace_size(B, H, N, HEAD_DIM, causal), 16)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def backward(q, k, v, o, do, lse, scale: float, causal: bool, stream=None, workspace=None):
+    """Allocate dQ, dK, dV (and the workspace) with torch and run fa_bwd."""
+    B, H, N, d = _shape(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        workspace = workspace_for(B, H, N, causal, q.device)
+    fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale, causal, workspace, stream)
+    return dq, dk, dv

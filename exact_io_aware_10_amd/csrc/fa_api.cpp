@@ -1,0 +1,86 @@
+// C ABI of libfa.so: argument validation and dispatch to the HIP kernels.
+// Declared in include/fa.h; every check runs before anything is launched.
+#include "fa.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kHeadDim = 128;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared shape/scalar checks.  Returns FA_OK, or the status to report.
+// *empty is set when there is nothing to compute (some of B, H, N is 0).
+int check_common(int B, int H, int N, int d, float scale, int causal, bool* empty) {
+  *empty = false;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (d != kHeadDim) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0 || N == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+  const int64_t elems = (int64_t)B * H * N * d;
+  if (elems >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, float scale, int causal, void* stream) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, causal, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_UNSUPPORTED;
+  hipError_t e = fa::launch_fwd(q, k, v, o, lse, B, H, N, scale, causal,
+                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal) {
+  bool empty = false;
+  if (check_common(B, H, N, d, 1.f, causal, &empty) != FA_OK) return 0;
+  if (empty) return 0;
+  const size_t delta = (size_t)B * H * N * sizeof(float);
+  return (delta + 255) & ~(size_t)255;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+           int causal, void* workspace, size_t workspace_bytes, void* stream) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, causal, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_bwd_workspace_size(B, H, N, d, causal);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  hipError_t e = fa::launch_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, causal,
+                                static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size, bad scale or causal flag)";
+    case FA_ERR_UNSUPPORTED: return "unsupported (head dim other than 128, misaligned pointer, or size overflow)";
+    case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than fa_bwd_workspace_size()";
+    case FA_ERR_HIP: return "HIP runtime rejected the launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

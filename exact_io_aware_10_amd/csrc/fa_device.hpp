@@ -1,0 +1,111 @@
+// Device-side building blocks shared by the gfx950 attention kernels:
+// vector types, bf16 MFMA wrappers, LDS tile addressing with an XOR swizzle,
+// the LDS transpose read, and cross-half-wave reductions.
+//
+// MFMA operand layouts (v_mfma_f32_32x32x16_bf16, wave64; lane l, h = l / 32):
+//   A (32 x 16, row m, col k): lane l holds A[l % 32][8h .. 8h + 7]
+//   B (16 x 32, row k, col n): lane l holds B[8h .. 8h + 7][l % 32]
+//   C (32 x 32): lane l holds element i (0..15) at
+//                row 8 (i / 4) + 4h + (i % 4), column l % 32
+// so a C tile read per lane is "column l % 32, a fixed set of 16 rows".  The
+// kernels compute transposed products (S^T = K Q^T, O^T = V^T P^T, ...) so
+// that each lane owns one query (or key) column and the softmax statistics of
+// a row stay inside one lane pair (l, l ^ 32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kD = 128;            // head dimension handled by every kernel
+constexpr int kRowBytes = kD * 2;  // one bf16 row of Q/K/V in bytes (256)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Physical 16-byte chunk of logical chunk c (0..15) in tile row r.  The map
+// is c ^ f(r) with f a bit permutation of r & 15 (bits b3 b2 b1 b0 ->
+// b3 b1 b0 b2), so
+//   * 16 consecutive rows reading one logical chunk hit 16 distinct chunks
+//     (row-wise MFMA operand reads), and
+//   * 4 consecutive rows (aligned to 4) reading two adjacent logical chunks
+//     hit 8 distinct chunks (the transpose reads).
+__device__ __forceinline__ int swz(int r) {
+  return (r & 8) | ((r & 3) << 1) | ((r >> 2) & 1);
+}
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ swz(row)) << 4);
+}
+// Byte offset of the 8-byte half `half` (0/1) of logical chunk `chunk`.
+__device__ __forceinline__ int tile_off8(int row, int chunk, int half) {
+  return tile_off(row, chunk) + (half << 3);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const char* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+__device__ __forceinline__ void lds_write16(char* base, int off, u32x4 v) {
+  *reinterpret_cast<u32x4*>(base + off) = v;
+}
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, source lane s supplies the address of 4 consecutive bf16; output
+// lane i receives element (i % 4) of the rows supplied by source lanes
+// (i / 4) + 4 j for j = 0..3.  With source lane s pointing at
+// T[r0 + s / 4][c0 + 4 (s % 4)], output lane i gets T[r0 + j][c0 + i], j=0..3.
+__device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 join(i16x4 lo, i16x4 hi) {
+  i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Value of x held by lane l ^ 32 combined with this lane's: max / sum over
+// the two half-waves (v_permlane32_swap).
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round-to-nearest-even float -> bf16 pair (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                        float a6, float a7) {
+  u32x4 u = {pack_bf16(a0, a1), pack_bf16(a2, a3), pack_bf16(a4, a5), pack_bf16(a6, a7)};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ u32x4 load16_or_zero(const char* p, bool ok) {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  if (ok) z = *reinterpret_cast<const u32x4*>(p);
+  return z;
+}
+
+}  // namespace fa

@@ -1,0 +1,240 @@
+// Forward kernel: exact softmax attention by tiling with an online softmax.
+//
+// One workgroup owns FWD_BR = 128 query rows of one (batch, head) and streams
+// the head's keys and values through LDS in tiles of FWD_BC = 64 rows; each
+// of its 4 wavefronts owns 32 of the query rows ("Interrogating the GPU,
+// part 5: FlashAttention", sections "How does tiling remove the traffic?" and
+// "What did FlashAttention-2 fix?": queries split across warps, outer loop
+// over query blocks, grid over query blocks x heads).
+//
+// Per tile and wave:
+//   S^T = K_j Q_i^T         bf16 MFMA 32x32x16, fp32 accumulate (C: key rows,
+//                           query columns; each lane owns one query)
+//   online softmax          m' = max(m, rowmax S), alpha = 2^(m - m'),
+//                           P = 2^(S log2e scale - m'), l = alpha l + rowsum P
+//                           ("How can you softmax a row you never see whole?",
+//                           update rule; exp2 with log2(e) folded into scale)
+//   O^T = alpha O^T + V_j^T P^T   bf16 MFMA; V read transposed from LDS
+// and after the last tile O = O / l (one division per row) and
+// LSE = ln2 (m + log2 l) ("What does the backward pass do without P?").
+// Causal: key tiles wholly after the workgroup's last query are never loaded,
+// tiles wholly after a wave's last query are skipped by that wave, and the
+// diagonal tiles are masked element-wise ("LLM flash attention", section
+// "End-to-end flow").
+#include "fa_device.hpp"
+#include "fa_internal.h"
+
+namespace fa {
+
+constexpr int FWD_BR = 128;
+constexpr int FWD_WAVES = 4;
+constexpr int FWD_QW = FWD_BR / FWD_WAVES;  // 32 query rows per wave
+constexpr int FWD_BC = 64;
+constexpr int FWD_TILE = FWD_BC * kRowBytes;  // 16 KiB per K or V tile
+constexpr int FWD_THREADS = FWD_WAVES * 64;
+constexpr int FWD_LOADS = FWD_TILE / 16 / FWD_THREADS;  // 16-byte chunks per thread
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v,
+                                                          uint16_t* __restrict__ o,
+                                                          float* __restrict__ lse, int BH, int N,
+                                                          int nqb, float sl2) {
+  // [buffer][K | V] tiles, each 64 rows x 256 bytes, swizzled (tile_off).
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * FWD_TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int h = lane >> 5;
+  const int col = lane & 31;
+
+  // Causal: issue the longest query blocks first.  Consecutive workgroups
+  // take consecutive heads of one query block.
+  const int id = blockIdx.x;
+  const int qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
+  const int bh = id % BH;
+  const int q0 = qb * FWD_BR;
+  const int q0w = q0 + wave * FWD_QW;
+  const int qrow = q0w + col;
+
+  const size_t head = (size_t)bh * (size_t)N * kD;
+  const char* qh = reinterpret_cast<const char*>(q + head);
+  const char* kh = reinterpret_cast<const char*>(k + head);
+  const char* vh = reinterpret_cast<const char*>(v + head);
+
+  // Q^T as the B operand: lane holds Q[qrow][16 kc + 8 h .. + 7].
+  bf16x8 qf[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc)
+    qf[kc] = __builtin_bit_cast(
+        bf16x8, load16_or_zero(qh + (size_t)qrow * kRowBytes + (2 * kc + h) * 16, qrow < N));
+
+  const int kend = CAUSAL ? min(N, q0 + FWD_BR) : N;
+  const int ntiles = (kend + FWD_BC - 1) / FWD_BC;
+
+  // Tile loader: thread tid moves chunks (row, chunk) = (tid / 16 + 16 i, tid % 16);
+  // 16 consecutive threads read one 256-byte row (coalesced).
+  const int ld_row = tid >> 4;
+  const int ld_chunk = tid & 15;
+  u32x4 kr[FWD_LOADS], vr[FWD_LOADS];
+  auto gload = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < FWD_LOADS; ++i) {
+      const int key = t * FWD_BC + ld_row + 16 * i;
+      const size_t off = (size_t)key * kRowBytes + ld_chunk * 16;
+      kr[i] = load16_or_zero(kh + off, key < N);
+      vr[i] = load16_or_zero(vh + off, key < N);
+    }
+  };
+  auto swrite = [&](int buf) {
+    char* kb = smem + buf * 2 * FWD_TILE;
+    char* vb = kb + FWD_TILE;
+#pragma unroll
+    for (int i = 0; i < FWD_LOADS; ++i) {
+      const int off = tile_off(ld_row + 16 * i, ld_chunk);
+      lds_write16(kb, off, kr[i]);
+      lds_write16(vb, off, vr[i]);
+    }
+  };
+
+  gload(0);
+  swrite(0);
+  __syncthreads();
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
+  float m = -INFINITY;  // running max, log2 domain of the scaled scores
+  float l = 0.f;        // running sum over this lane's half of each tile
+
+  // Transpose-read addressing for V (see lds_read_tr): 16-lane group of dims.
+  const int tr_s = lane & 15;
+  const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (tr_s & 3);  // + 32 mb
+  const int tr_row = 4 * h + (tr_s >> 2);                      // + 32 st + 16 u (+ 8)
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) gload(t + 1);
+    const int k0 = t * FWD_BC;
+    const bool active = !CAUSAL || (k0 <= q0w + FWD_QW - 1);
+    if (active) {
+      const char* kb = smem + buf * 2 * FWD_TILE;
+      const char* vb = kb + FWD_TILE;
+
+      f32x16 s[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+#pragma unroll
+        for (int kc = 0; kc < 8; ++kc) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, lds_read16(kb, tile_off(32 * st + col, 2 * kc + h)));
+          s[st] = mfma32(a, qf[kc], s[st]);
+        }
+      }
+
+      const bool need_mask = (CAUSAL && (k0 + FWD_BC - 1 > q0w)) || (k0 + FWD_BC > N);
+      if (need_mask) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * st + 8 * (i >> 2) + 4 * h + (i & 3);
+            if (key >= N || (CAUSAL && key > qrow)) s[st][i] = -INFINITY;
+          }
+      }
+
+      float mx = s[0][0];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
+      mx = halves_max(mx);
+      const float mnew = fmaxf(m, mx * sl2);
+      const float mu = (mnew == -INFINITY) ? 0.f : mnew;  // no (-inf) - (-inf)
+      const float alpha = fast_exp2(m - mu);
+      float rs = 0.f;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(__builtin_fmaf(s[st][i], sl2, -mu));
+          s[st][i] = p;
+          rs += p;
+        }
+      l = l * alpha + rs;
+      m = mnew;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mb][i] *= alpha;
+
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int b = 8 * u;
+          pb[st][u] = pack8(s[st][b], s[st][b + 1], s[st][b + 2], s[st][b + 3], s[st][b + 4],
+                            s[st][b + 5], s[st][b + 6], s[st][b + 7]);
+        }
+
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int dim = 32 * mb + tr_dim;
+        const int chunk = dim >> 3;
+        const int half = (dim >> 2) & 1;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 32 * st + 16 * u + tr_row;
+            const i16x4 lo = lds_read_tr(vb + tile_off8(r, chunk, half));
+            const i16x4 hi = lds_read_tr(vb + tile_off8(r + 8, chunk, half));
+            acc[mb] = mfma32(join(lo, hi), pb[st][u], acc[mb]);
+          }
+      }
+    }
+    if (t + 1 < ntiles) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float lt = halves_sum(l);
+  if (qrow < N) {
+    const float inv = 1.f / lt;
+    char* orow = reinterpret_cast<char*>(o + head) + (size_t)qrow * kRowBytes;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int i = 4 * g;
+        u32x2 w = {pack_bf16(acc[mb][i] * inv, acc[mb][i + 1] * inv),
+                   pack_bf16(acc[mb][i + 2] * inv, acc[mb][i + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + (32 * mb + 8 * g + 4 * h) * 2) = w;
+      }
+    if (h == 0) lse[(size_t)bh * N + qrow] = (m + __log2f(lt)) * kLn2;
+  }
+}
+
+hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int N, float scale, int causal, hipStream_t stream) {
+  const int BH = B * H;
+  const int nqb = (N + FWD_BR - 1) / FWD_BR;
+  const float sl2 = scale * kLog2e;
+  dim3 grid((unsigned)(nqb * BH)), block(FWD_THREADS);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  uint16_t* oo = static_cast<uint16_t*>(o);
+  if (causal)
+    hipLaunchKernelGGL(fwd_kernel<true>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2);
+  else
+    hipLaunchKernelGGL(fwd_kernel<false>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2);
+  return hipGetLastError();
+}
+
+}  // namespace fa

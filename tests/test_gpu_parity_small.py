@@ -1,0 +1,62 @@
+"""GPU parity against the fp64 oracle on small shapes: every tail and tile
+boundary, causal and not, one and several heads.  Calls go through the C ABI
+(ctypes binding of libfa.so)."""
+import math
+
+import numpy as np
+import pytest
+
+import fa_inputs
+from oracle import attention as ora
+from tests.gpu_helpers import TOL_LSE, TOL_OUT, f64, from_dev, max_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NS = [1, 2, 3, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 1000]
+
+
+@pytest.fixture(scope="module")
+def fa():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_io_aware_10_amd as fa
+    fa.load_library()
+    return fa
+
+
+@pytest.mark.parametrize("N", NS)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("BH", [(1, 1), (1, 3)])
+def test_forward_small(fa, N, causal, BH):
+    import torch
+    B, H = BH
+    x = fa_inputs.make(B, H, N, seed=7000 + N + 100 * causal + 10 * H)
+    scale = fa_inputs.SCALE
+    q, k, v = (to_dev(x[n], torch) for n in "qkv")
+    o, lse = fa.forward(q, k, v, scale, causal)
+    torch.cuda.synchronize()
+    ro, rl = ora.forward(f64(x["q"]), f64(x["k"]), f64(x["v"]), scale, causal)
+    eo, el = max_err(from_dev(o), ro), max_err(from_dev(lse), rl)
+    print(f"fwd N={N} causal={causal} BH={BH}: O err {eo:.2e} LSE err {el:.2e}", flush=True)
+    assert eo <= TOL_OUT and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("N", NS)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("BH", [(1, 1), (1, 3)])
+def test_backward_small(fa, N, causal, BH):
+    import torch
+    B, H = BH
+    x = fa_inputs.make(B, H, N, seed=8000 + N + 100 * causal + 10 * H, with_do=True)
+    scale = fa_inputs.SCALE
+    q, k, v, do = (to_dev(x[n], torch) for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, scale, causal)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, scale, causal)
+    torch.cuda.synchronize()
+    Q, K, V, DO = (f64(x[n]) for n in ("q", "k", "v", "do"))
+    ro, _ = ora.forward(Q, K, V, scale, causal)
+    rdq, rdk, rdv, _ = ora.backward(Q, K, V, ro, DO, scale, causal)
+    e = [max_err(from_dev(a), b) for a, b in ((dq, rdq), (dk, rdk), (dv, rdv))]
+    print(f"bwd N={N} causal={causal} BH={BH}: dQ {e[0]:.2e} dK {e[1]:.2e} dV {e[2]:.2e}", flush=True)
+    assert max(e) <= TOL_OUT
