@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Throughput of the exact-attention hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input:
+  fa_fwd (O, LSE)  ->  fa_bwd_preprocess (D)  ->  fa_bwd_dkdv  ->  fa_bwd_dq
+on B=1, H=64, N=8192, d=128, causal, bf16 (the N = 8192 workload the
+throughput target is stated at; forward-only workloads can be selected with
+--workload).  Inputs are seeded iid N(0,1) bf16 tensors already resident in
+device memory when the timed region starts.
+
+Prints ONE JSON line on stdout.  `value` is the step's credited TFLOP/s
+(forward 4 N^2 d B H, backward 2.5x that, both halved when causal); the
+per-kernel durations come from HIP events recorded on the launch stream
+around every kernel of every timed step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import fa_inputs  # noqa: E402
+from exact_io_aware_10_amd import accounting as acc  # noqa: E402
+
+METRIC = "attention fwd/bwd TFLOP/s at d=128 bf16, % of MI355X dense bf16 MFMA peak"
+KERNEL_FILES = ("fa_device.hpp", "fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp", "fa_internal.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_FILES:
+        with open(os.path.join(ROOT, "exact_io_aware_10_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if they were taken
+    on the current kernel sources (profiles/traffic.json), else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = data.get(f"{kernel}@{workload}")
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(x, w, heads: int):
+    """The fp64 oracle (forward + backward) on the first `heads` heads."""
+    import numpy as np
+    from oracle import attention as ora
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()
+                     if p.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        cores = 1
+    sl = (slice(0, 1), slice(0, heads))
+    Q, K, V = (fa_inputs.bf16_bits_to_f64(x[n][sl]) for n in "qkv")
+    has_bwd = "do" in x
+    t0 = time.perf_counter()
+    o, _ = ora.forward(Q, K, V, fa_inputs.SCALE, w["causal"])
+    flops = acc.fwd_flops(1, heads, w["N"], 128, w["causal"])
+    if has_bwd:
+        DO = fa_inputs.bf16_bits_to_f64(x["do"][sl])
+        ora.backward(Q, K, V, o, DO, fa_inputs.SCALE, w["causal"])
+        flops += acc.bwd_flops(1, heads, w["N"], 128, w["causal"])
+    dt = time.perf_counter() - t0
+    del np
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle {'forward+backward' if has_bwd else 'forward'} on heads 0-{heads - 1} "
+                   f"of the same workload (batch 0), {dt:.1f} s wall; credited FLOPs of that sample"),
+        "seconds": dt,
+        "host_cpu": platform.processor() or platform.machine(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="causal_b1_h64_n8192", choices=sorted(fa_inputs.WORKLOADS))
+    ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle timing sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(heads are independent, so several GPUs would each run this same kernel "
+              "on their own share of heads; see the sharding note in the design document).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_io_aware_10_amd as fa
+
+    w = fa_inputs.WORKLOADS[args.workload]
+    B, H, N, causal = w["B"], w["H"], w["N"], w["causal"]
+    d = fa_inputs.HEAD_DIM
+    with_bwd = w["bwd"]
+    scale = fa_inputs.SCALE
+    log(f"workload {args.workload}: B={B} H={H} N={N} d={d} causal={causal} bwd={with_bwd}")
+
+    x = fa_inputs.make_workload(args.workload, with_do=with_bwd)
+    dev = torch.device("cuda:0")
+
+    def put(bits):
+        import numpy as np
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = put(x["q"]), put(x["k"]), put(x["v"])
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if with_bwd:
+        do = put(x["do"])
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    names = ["fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if with_bwd else [])
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fwd(q, k, v, o, lse, scale, causal, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if with_bwd:
+            fa.fa_bwd_preprocess(o, do, delta, stream)
+            if ev is not None:
+                ev[2].record(stream)
+            fa.fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, scale, causal, stream)
+            if ev is not None:
+                ev[3].record(stream)
+            fa.fa_bwd_dq(q, k, v, do, lse, delta, dq, scale, causal, stream)
+            if ev is not None:
+                ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    kern_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; per kernel (ms): "
+        + ", ".join(f"{n} {t:.3f}" for n, t in kern_ms.items()))
+
+    peak = acc.MI355X_BF16_DENSE_TFLOPS
+    fwd_f = acc.fwd_flops(B, H, N, d, causal)
+    bwd_f = acc.bwd_flops(B, H, N, d, causal) if with_bwd else 0.0
+    step_f = fwd_f + bwd_f
+    value = step_f / (ms_per_step * 1e-3) / 1e12
+    fwd_tf = fwd_f / (kern_ms["fwd"] * 1e-3) / 1e12
+    out_extra = {
+        "fwd_ms": kern_ms["fwd"],
+        "fwd_tflops": fwd_tf,
+        "fwd_frac_of_peak": fwd_tf / peak,
+        "fwd_hbm_gbps": acc.fwd_bytes(B, H, N, d) / (kern_ms["fwd"] * 1e-3) / 1e9,
+    }
+    if with_bwd:
+        bwd_ms = kern_ms["bwd_pre"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
+        bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
+        out_extra.update({"bwd_ms": bwd_ms, "bwd_tflops": bwd_tf, "bwd_frac_of_peak": bwd_tf / peak,
+                          "kernel_ms": kern_ms})
+
+    # Roofline of the kernel that takes the most time per step.
+    half = 0.5 if causal else 1.0
+    per_head_mm = 2.0 * N * N * d * half  # one N x N x d matmul, causal-halved
+    work = {
+        "fwd": ("mfma", 2 * per_head_mm * B * H, "fa_fwd: S = Q K^T and O = P V"),
+        "bwd_pre": ("hbm", acc.bwd_pre_bytes(B, H, N, d), "fa_bwd_preprocess: read O, dO; write D"),
+        "bwd_dkdv": ("mfma", 4 * per_head_mm * B * H, "fa_bwd_dkdv: S, dP, dV, dK matmuls"),
+        "bwd_dq": ("mfma", 3 * per_head_mm * B * H, "fa_bwd_dq: S, dP, dQ matmuls"),
+    }
+    dom = max(names, key=lambda n: kern_ms[n])
+    bound, units, what = work[dom]
+    if bound == "mfma":
+        achieved = units / (kern_ms[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak}
+    else:
+        achieved = units / (kern_ms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": acc.MI355X_HBM_GBPS, "unit": "GB/s",
+                "frac": achieved / acc.MI355X_HBM_GBPS}
+    roof["traffic"] = traffic_for(dom, args.workload)
+    roof["kernel"] = dom
+    roof["work_per_launch"] = units
+    roof["work"] = what
+    roof["avg_launch_ms"] = kern_ms[dom]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the fp64 oracle on {args.cpu_heads} heads ...")
+        cpu = cpu_baseline(x, w, args.cpu_heads)
+        log(f"oracle: {cpu['seconds']:.1f} s, {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded iid N(0,1) bf16 Q, K, V, dO",
+        "config": {"workload": args.workload + ("_fwd_bwd" if with_bwd else "_fwd"), "B": B, "H": H,
+                   "N": N, "d": d, "causal": causal, "scale": scale},
+        "frac_of_peak": value / peak,
+        "peak_tflops": peak,
+        **out_extra,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

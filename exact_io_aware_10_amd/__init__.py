@@ -8,6 +8,9 @@ built, or the tensors are not on a ROCm device, the calls raise.
 Functions mirror the C entry points:
   fa_fwd(q, k, v, o, lse, scale, causal)                       -> None
   fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale, causal, ws)   -> None
+  fa_bwd_preprocess(o, dO, delta)                              -> None
+  fa_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, scale, causal)  -> None
+  fa_bwd_dq(q, k, v, dO, lse, delta, dq, scale, causal)        -> None
   fa_bwd_workspace_size(B, H, N, d, causal)                    -> int
   fa_strerror(status)                                          -> str
 plus allocating conveniences forward(...) and backward(...).
@@ -52,6 +55,12 @@ def load_library() -> ctypes.CDLL:
         lib.fa_bwd_workspace_size.restype = sz
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
         lib.fa_bwd.restype = i
+        lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp]
+        lib.fa_bwd_preprocess.restype = i
+        lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_bwd_dkdv.restype = i
+        lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_bwd_dq.restype = i
         lib.fa_strerror.argtypes = [i]
         lib.fa_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -119,6 +128,42 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, workspac
     st = load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                                _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
                                _ptr(workspace), nbytes, _stream(stream))
+    if st != FA_OK:
+        raise FAError(st)
+
+
+def fa_bwd_preprocess(o, do, delta, stream=None) -> None:
+    B, H, N, d = _shape(o)
+    _check_tensor("o", o, torch.bfloat16, (B, H, N, d))
+    _check_tensor("dO", do, torch.bfloat16, (B, H, N, d))
+    _check_tensor("delta", delta, torch.float32, (B, H, N))
+    st = load_library().fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(delta), B, H, N, d, _stream(stream))
+    if st != FA_OK:
+        raise FAError(st)
+
+
+def fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, scale: float, causal: bool, stream=None) -> None:
+    B, H, N, d = _shape(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("dO", do), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, torch.bfloat16, (B, H, N, d))
+    _check_tensor("lse", lse, torch.float32, (B, H, N))
+    _check_tensor("delta", delta, torch.float32, (B, H, N))
+    st = load_library().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta),
+                                     _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
+                                     _stream(stream))
+    if st != FA_OK:
+        raise FAError(st)
+
+
+def fa_bwd_dq(q, k, v, do, lse, delta, dq, scale: float, causal: bool, stream=None) -> None:
+    B, H, N, d = _shape(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("dO", do), ("dq", dq)):
+        _check_tensor(name, t, torch.bfloat16, (B, H, N, d))
+    _check_tensor("lse", lse, torch.float32, (B, H, N))
+    _check_tensor("delta", delta, torch.float32, (B, H, N))
+    st = load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta),
+                                   _ptr(dq), B, H, N, d, float(scale), int(bool(causal)),
+                                   _stream(stream))
     if st != FA_OK:
         raise FAError(st)
 

@@ -55,6 +55,47 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal) {
   return (delta + 255) & ~(size_t)255;
 }
 
+int fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int H, int N, int d,
+                      void* stream) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, 1.f, 0, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!o || !dO || !delta) return FA_ERR_INVALID_ARG;
+  if (!aligned16(o) || !aligned16(dO) || !aligned16(delta)) return FA_ERR_UNSUPPORTED;
+  hipError_t e = fa::launch_bwd_pre(o, dO, delta, B, H, N, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                const float* delta, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                int causal, void* stream) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, causal, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!q || !k || !v || !dO || !lse || !delta || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) ||
+      !aligned16(delta) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_UNSUPPORTED;
+  hipError_t e = fa::launch_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, B, H, N, scale, causal,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+              const float* delta, void* dq, int B, int H, int N, int d, float scale, int causal,
+              void* stream) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, causal, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!q || !k || !v || !dO || !lse || !delta || !dq) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) ||
+      !aligned16(delta) || !aligned16(dq))
+    return FA_ERR_UNSUPPORTED;
+  hipError_t e = fa::launch_bwd_dq(q, k, v, dO, lse, delta, dq, B, H, N, scale, causal,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
            const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
            int causal, void* workspace, size_t workspace_bytes, void* stream) {
@@ -67,8 +108,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     return FA_ERR_UNSUPPORTED;
   const size_t need = fa_bwd_workspace_size(B, H, N, d, causal);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
-  hipError_t e = fa::launch_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, causal,
-                                static_cast<float*>(workspace), static_cast<hipStream_t>(stream));
+  float* delta = static_cast<float*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = fa::launch_bwd_pre(o, dO, delta, B, H, N, s);
+  if (e == hipSuccess)
+    e = fa::launch_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, B, H, N, scale, causal, s);
+  if (e == hipSuccess) e = fa::launch_bwd_dq(q, k, v, dO, lse, delta, dq, B, H, N, scale, causal, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -400,42 +400,42 @@ __global__ __launch_bounds__(DQ_THREADS) void bwd_dq_kernel(
   }
 }
 
-hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                      const float* lse, void* dq, void* dk, void* dv, int B, int H, int N,
-                      float scale, int causal, float* delta, hipStream_t stream) {
-  const int BH = B * H;
-  const int rows = BH * N;
-  const float sl2 = scale * kLog2e;
-  const uint16_t* qq = static_cast<const uint16_t*>(q);
-  const uint16_t* kk = static_cast<const uint16_t*>(k);
-  const uint16_t* vv = static_cast<const uint16_t*>(v);
-  const uint16_t* oo = static_cast<const uint16_t*>(o);
-  const uint16_t* dd = static_cast<const uint16_t*>(dO);
-
+hipError_t launch_bwd_pre(const void* o, const void* dO, float* delta, int B, int H, int N,
+                          hipStream_t stream) {
+  const int rows = B * H * N;
   hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0,
-                     stream, oo, dd, delta, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+                     stream, static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dO),
+                     delta, rows);
+  return hipGetLastError();
+}
 
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                           const float* lse, const float* delta, void* dk, void* dv, int B, int H,
+                           int N, float scale, int causal, hipStream_t stream) {
+  const int BH = B * H;
+  const float sl2 = scale * kLog2e;
   const int nkb = (N + KV_BK - 1) / KV_BK;
-  dim3 gkv((unsigned)(nkb * BH)), bkv(KV_THREADS);
-  if (causal)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<true>, gkv, bkv, 0, stream, qq, kk, vv, dd, lse, delta,
-                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), BH, N, sl2, scale);
-  else
-    hipLaunchKernelGGL(bwd_dkdv_kernel<false>, gkv, bkv, 0, stream, qq, kk, vv, dd, lse, delta,
-                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), BH, N, sl2, scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  dim3 grid((unsigned)(nkb * BH)), block(KV_THREADS);
+  auto kern = causal ? bwd_dkdv_kernel<true> : bwd_dkdv_kernel<false>;
+  hipLaunchKernelGGL(kern, grid, block, 0, stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                     static_cast<const uint16_t*>(dO), lse, delta, static_cast<uint16_t*>(dk),
+                     static_cast<uint16_t*>(dv), BH, N, sl2, scale);
+  return hipGetLastError();
+}
 
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+                         const float* lse, const float* delta, void* dq, int B, int H, int N,
+                         float scale, int causal, hipStream_t stream) {
+  const int BH = B * H;
+  const float sl2 = scale * kLog2e;
   const int nqb = (N + DQ_BQ - 1) / DQ_BQ;
-  dim3 gq((unsigned)(nqb * BH)), bq(DQ_THREADS);
-  if (causal)
-    hipLaunchKernelGGL(bwd_dq_kernel<true>, gq, bq, 0, stream, qq, kk, vv, dd, lse, delta,
-                       static_cast<uint16_t*>(dq), BH, N, nqb, sl2, scale);
-  else
-    hipLaunchKernelGGL(bwd_dq_kernel<false>, gq, bq, 0, stream, qq, kk, vv, dd, lse, delta,
-                       static_cast<uint16_t*>(dq), BH, N, nqb, sl2, scale);
+  dim3 grid((unsigned)(nqb * BH)), block(DQ_THREADS);
+  auto kern = causal ? bwd_dq_kernel<true> : bwd_dq_kernel<false>;
+  hipLaunchKernelGGL(kern, grid, block, 0, stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                     static_cast<const uint16_t*>(dO), lse, delta, static_cast<uint16_t*>(dq), BH,
+                     N, nqb, sl2, scale);
   return hipGetLastError();
 }
 

@@ -87,6 +87,30 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            int B, int H, int N, int d, float scale, int causal,
            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The three stages fa_bwd runs, in order, on one stream.  Each is exposed so a
+ * caller can schedule or time them separately; running all three with the
+ * same arguments is exactly fa_bwd.  Arguments as for fa_bwd; delta is a
+ * device buffer of B*H*N float32 (16-byte aligned), written by
+ * fa_bwd_preprocess and read by the other two.
+ *
+ * fa_bwd_preprocess: delta_i = D_i = sum_k dO_ik O_ik, the row sum of dO o O
+ *   that plays the role of delta in dS = P o (dP - delta) ("Interrogating
+ *   the GPU, part 5", section "What does the backward pass do without P?").
+ * fa_bwd_dkdv: for each key block, recompute P = exp(scale q.k - L) over all
+ *   visible queries and accumulate dV = P^T dO and dK = scale dS^T Q.
+ * fa_bwd_dq: for each query block, recompute P and dS over all visible keys
+ *   and accumulate dQ = scale dS K.
+ */
+int fa_bwd_preprocess(const void* o, const void* dO, float* delta,
+                      int B, int H, int N, int d, void* stream);
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                const float* lse, const float* delta, void* dk, void* dv,
+                int B, int H, int N, int d, float scale, int causal, void* stream);
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
+              const float* lse, const float* delta, void* dq,
+              int B, int H, int N, int d, float scale, int causal, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_strerror(int status);
 
