@@ -102,6 +102,23 @@ __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, 
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// Buffer resource over [base, base + bytes): loads past the end return zero
+// (and, for the LDS-direct form, write zero), so tails need no branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit dwords, gfx9 family
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+}
+// 16 bytes per lane from global memory straight into LDS: lane i writes
+// lds_base + 16 i (lds_base must be wave-uniform).
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, char* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                           voff, 0, 0, 0);
+}
+
 __device__ __forceinline__ u32x4 load16_or_zero(const char* p, bool ok) {
   u32x4 z = {0u, 0u, 0u, 0u};
   if (ok) z = *reinterpret_cast<const u32x4*>(p);

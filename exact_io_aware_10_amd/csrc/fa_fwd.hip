@@ -32,15 +32,20 @@ constexpr int FWD_QW = FWD_BR / FWD_WAVES;  // 32 query rows per wave
 constexpr int FWD_BC = 64;
 constexpr int FWD_TILE = FWD_BC * kRowBytes;  // 16 KiB per K or V tile
 constexpr int FWD_THREADS = FWD_WAVES * 64;
-constexpr int FWD_LOADS = FWD_TILE / 16 / FWD_THREADS;  // 16-byte chunks per thread
+constexpr int FWD_LOADS = FWD_TILE / 1024 / FWD_WAVES;  // 1 KiB LDS-direct loads per wave
+
+// Rows whose running maximum grows by less than this (log2 units) keep the
+// stale maximum: P is then bounded by 2^kTau and the O / l rescale is skipped
+// ("Interrogating the GPU, part 5", FlashAttention-4 section: the rescale
+// becomes conditional; exact in real arithmetic since O and l share the
+// reference maximum that LSE records).
+constexpr float kTau = 8.f;
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(const uint16_t* __restrict__ q,
-                                                          const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v,
-                                                          uint16_t* __restrict__ o,
-                                                          float* __restrict__ lse, int BH, int N,
-                                                          int nqb, float sl2) {
+__global__ __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
+                float* __restrict__ lse, int BH, int N, int nqb, float sl2) {
   // [buffer][K | V] tiles, each 64 rows x 256 bytes, swizzled (tile_off).
   __shared__ __attribute__((aligned(16))) char smem[2 * 2 * FWD_TILE];
 
@@ -60,47 +65,40 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(const uint16_t* __rest
   const int qrow = q0w + col;
 
   const size_t head = (size_t)bh * (size_t)N * kD;
-  const char* qh = reinterpret_cast<const char*>(q + head);
-  const char* kh = reinterpret_cast<const char*>(k + head);
-  const char* vh = reinterpret_cast<const char*>(v + head);
+  const uint32_t head_bytes = (uint32_t)N * kRowBytes;
+  const rsrc_t rq = make_rsrc(q + head, head_bytes);
+  const rsrc_t rk = make_rsrc(k + head, head_bytes);
+  const rsrc_t rv = make_rsrc(v + head, head_bytes);
 
-  // Q^T as the B operand: lane holds Q[qrow][16 kc + 8 h .. + 7].
+  // Q^T as the B operand: lane holds Q[qrow][16 kc + 8 h .. + 7] (zero past N).
   bf16x8 qf[8];
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc)
-    qf[kc] = __builtin_bit_cast(
-        bf16x8, load16_or_zero(qh + (size_t)qrow * kRowBytes + (2 * kc + h) * 16, qrow < N));
+    qf[kc] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)qrow * kRowBytes + (2 * kc + h) * 16));
 
   const int kend = CAUSAL ? min(N, q0 + FWD_BR) : N;
   const int ntiles = (kend + FWD_BC - 1) / FWD_BC;
 
-  // Tile loader: thread tid moves chunks (row, chunk) = (tid / 16 + 16 i, tid % 16);
-  // 16 consecutive threads read one 256-byte row (coalesced).
-  const int ld_row = tid >> 4;
-  const int ld_chunk = tid & 15;
-  u32x4 kr[FWD_LOADS], vr[FWD_LOADS];
-  auto gload = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < FWD_LOADS; ++i) {
-      const int key = t * FWD_BC + ld_row + 16 * i;
-      const size_t off = (size_t)key * kRowBytes + ld_chunk * 16;
-      kr[i] = load16_or_zero(kh + off, key < N);
-      vr[i] = load16_or_zero(vh + off, key < N);
-    }
-  };
-  auto swrite = [&](int buf) {
+  // Tile loader: LDS-direct buffer loads.  Instruction n of wave w fills rows
+  // 16 n + 4 w .. + 3 (1 KiB, lane-linear in LDS); lane i lands on physical
+  // chunk i % 16 of its row and so fetches the logical chunk stored there.
+  const int ld_sub = lane >> 4;
+  const int ld_pc = lane & 15;
+  auto issue_tile = [&](int t, int buf) {
     char* kb = smem + buf * 2 * FWD_TILE;
     char* vb = kb + FWD_TILE;
 #pragma unroll
-    for (int i = 0; i < FWD_LOADS; ++i) {
-      const int off = tile_off(ld_row + 16 * i, ld_chunk);
-      lds_write16(kb, off, kr[i]);
-      lds_write16(vb, off, vr[i]);
+    for (int n = 0; n < FWD_LOADS; ++n) {
+      const int row0 = 16 * n + 4 * wave;
+      const int row = row0 + ld_sub;
+      const uint32_t voff = (uint32_t)(t * FWD_BC + row) * kRowBytes + ((ld_pc ^ swz(row)) << 4);
+      buf_load16_lds(rk, kb + row0 * kRowBytes, voff);
+      buf_load16_lds(rv, vb + row0 * kRowBytes, voff);
     }
   };
 
-  gload(0);
-  swrite(0);
+  issue_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   f32x16 acc[4];
@@ -108,7 +106,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(const uint16_t* __rest
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
-  float m = -INFINITY;  // running max, log2 domain of the scaled scores
+  float m = -INFINITY;  // reference maximum, log2 domain of the scaled scores
   float l = 0.f;        // running sum over this lane's half of each tile
 
   // Transpose-read addressing for V (see lds_read_tr): 16-lane group of dims.
@@ -118,7 +116,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(const uint16_t* __rest
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
+    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
     const int k0 = t * FWD_BC;
     const bool active = !CAUSAL || (k0 <= q0w + FWD_QW - 1);
     if (active) {
@@ -154,9 +152,19 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(const uint16_t* __rest
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
       mx = halves_max(mx);
-      const float mnew = fmaxf(m, mx * sl2);
-      const float mu = (mnew == -INFINITY) ? 0.f : mnew;  // no (-inf) - (-inf)
-      const float alpha = fast_exp2(m - mu);
+      const float mcand = mx * sl2;
+      if (__builtin_amdgcn_ballot_w64(mcand > m + kTau) != 0) {
+        const float mnew = fmaxf(m, mcand);
+        const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m - mnew);
+        m = mnew;
+        l *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[mb][i] *= alpha;
+      }
+      const float mu = (m == -INFINITY) ? 0.f : m;  // no (-inf) - (-inf)
+
       float rs = 0.f;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
@@ -166,12 +174,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(const uint16_t* __rest
           s[st][i] = p;
           rs += p;
         }
-      l = l * alpha + rs;
-      m = mnew;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mb][i] *= alpha;
+      l += rs;
 
       bf16x8 pb[2][2];
 #pragma unroll
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(FWD_THREADS) void fwd_kernel(const uint16_t* __rest
           }
       }
     }
-    if (t + 1 < ntiles) swrite(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
