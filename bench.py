@@ -133,7 +133,7 @@ def main():
     if with_bwd:
         do = put(x["do"])
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-        delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        ws = fa.workspace_for(B, H, N, causal, dev)
     stream = torch.cuda.current_stream()
     names = ["fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if with_bwd else [])
 
@@ -144,13 +144,13 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         if with_bwd:
-            fa.fa_bwd_preprocess(o, do, delta, stream)
+            fa.fa_bwd_preprocess(o, do, lse, ws, stream)
             if ev is not None:
                 ev[2].record(stream)
-            fa.fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, scale, causal, stream)
+            fa.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, scale, causal, stream)
             if ev is not None:
                 ev[3].record(stream)
-            fa.fa_bwd_dq(q, k, v, do, lse, delta, dq, scale, causal, stream)
+            fa.fa_bwd_dq(q, k, v, do, ws, dq, scale, causal, stream)
             if ev is not None:
                 ev[4].record(stream)
 
@@ -195,7 +195,7 @@ def main():
     per_head_mm = 2.0 * N * N * d * half  # one N x N x d matmul, causal-halved
     work = {
         "fwd": ("mfma", 2 * per_head_mm * B * H, "fa_fwd: S = Q K^T and O = P V"),
-        "bwd_pre": ("hbm", acc.bwd_pre_bytes(B, H, N, d), "fa_bwd_preprocess: read O, dO; write D"),
+        "bwd_pre": ("hbm", acc.bwd_pre_bytes(B, H, N, d), "fa_bwd_preprocess: read O, dO, LSE; write D, L log2e"),
         "bwd_dkdv": ("mfma", 4 * per_head_mm * B * H, "fa_bwd_dkdv: S, dP, dV, dK matmuls"),
         "bwd_dq": ("mfma", 3 * per_head_mm * B * H, "fa_bwd_dq: S, dP, dQ matmuls"),
     }

@@ -8,9 +8,9 @@ built, or the tensors are not on a ROCm device, the calls raise.
 Functions mirror the C entry points:
   fa_fwd(q, k, v, o, lse, scale, causal)                       -> None
   fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale, causal, ws)   -> None
-  fa_bwd_preprocess(o, dO, delta)                              -> None
-  fa_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, scale, causal)  -> None
-  fa_bwd_dq(q, k, v, dO, lse, delta, dq, scale, causal)        -> None
+  fa_bwd_preprocess(o, dO, lse, ws)                            -> None
+  fa_bwd_dkdv(q, k, v, dO, ws, dk, dv, scale, causal)          -> None
+  fa_bwd_dq(q, k, v, dO, ws, dq, scale, causal)                -> None
   fa_bwd_workspace_size(B, H, N, d, causal)                    -> int
   fa_strerror(status)                                          -> str
 plus allocating conveniences forward(...) and backward(...).
@@ -55,11 +55,11 @@ def load_library() -> ctypes.CDLL:
         lib.fa_bwd_workspace_size.restype = sz
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
         lib.fa_bwd.restype = i
-        lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp]
+        lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, vp]
         lib.fa_bwd_preprocess.restype = i
-        lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, f, i, vp]
         lib.fa_bwd_dkdv.restype = i
-        lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, f, i, vp]
         lib.fa_bwd_dq.restype = i
         lib.fa_strerror.argtypes = [i]
         lib.fa_strerror.restype = ctypes.c_char_p
@@ -132,38 +132,42 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, workspac
         raise FAError(st)
 
 
-def fa_bwd_preprocess(o, do, delta, stream=None) -> None:
+def _ws(workspace):
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def fa_bwd_preprocess(o, do, lse, workspace, stream=None) -> None:
     B, H, N, d = _shape(o)
     _check_tensor("o", o, torch.bfloat16, (B, H, N, d))
     _check_tensor("dO", do, torch.bfloat16, (B, H, N, d))
-    _check_tensor("delta", delta, torch.float32, (B, H, N))
-    st = load_library().fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(delta), B, H, N, d, _stream(stream))
+    _check_tensor("lse", lse, torch.float32, (B, H, N))
+    wp, wn = _ws(workspace)
+    st = load_library().fa_bwd_preprocess(_ptr(o), _ptr(do), _ptr(lse), wp, wn, B, H, N, d,
+                                          _stream(stream))
     if st != FA_OK:
         raise FAError(st)
 
 
-def fa_bwd_dkdv(q, k, v, do, lse, delta, dk, dv, scale: float, causal: bool, stream=None) -> None:
+def fa_bwd_dkdv(q, k, v, do, workspace, dk, dv, scale: float, causal: bool, stream=None) -> None:
     B, H, N, d = _shape(q)
     for name, t in (("q", q), ("k", k), ("v", v), ("dO", do), ("dk", dk), ("dv", dv)):
         _check_tensor(name, t, torch.bfloat16, (B, H, N, d))
-    _check_tensor("lse", lse, torch.float32, (B, H, N))
-    _check_tensor("delta", delta, torch.float32, (B, H, N))
-    st = load_library().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta),
-                                     _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
-                                     _stream(stream))
+    wp, wn = _ws(workspace)
+    st = load_library().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), wp, wn, _ptr(dk), _ptr(dv),
+                                     B, H, N, d, float(scale), int(bool(causal)), _stream(stream))
     if st != FA_OK:
         raise FAError(st)
 
 
-def fa_bwd_dq(q, k, v, do, lse, delta, dq, scale: float, causal: bool, stream=None) -> None:
+def fa_bwd_dq(q, k, v, do, workspace, dq, scale: float, causal: bool, stream=None) -> None:
     B, H, N, d = _shape(q)
     for name, t in (("q", q), ("k", k), ("v", v), ("dO", do), ("dq", dq)):
         _check_tensor(name, t, torch.bfloat16, (B, H, N, d))
-    _check_tensor("lse", lse, torch.float32, (B, H, N))
-    _check_tensor("delta", delta, torch.float32, (B, H, N))
-    st = load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta),
-                                   _ptr(dq), B, H, N, d, float(scale), int(bool(causal)),
-                                   _stream(stream))
+    wp, wn = _ws(workspace)
+    st = load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), wp, wn, _ptr(dq), B, H, N, d,
+                                   float(scale), int(bool(causal)), _stream(stream))
     if st != FA_OK:
         raise FAError(st)
 

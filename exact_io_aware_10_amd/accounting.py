@@ -37,8 +37,9 @@ def bwd_bytes(B: int, H: int, N: int, d: int) -> float:
 
 
 def bwd_pre_bytes(B: int, H: int, N: int, d: int) -> float:
-    """D = rowsum(dO * O): read O and dO, write D: 4 N d + 4 N per head."""
-    return float(B * H * (2 * N * d * BF16 + N * FP32))
+    """D = rowsum(dO * O) and L log2(e): read O, dO and L, write D and
+    L log2(e): 4 N d + 12 N bytes per head."""
+    return float(B * H * (2 * N * d * BF16 + 3 * N * FP32))
 
 
 def naive_intensity(N: int, d: int) -> float:

@@ -51,48 +51,56 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal) {
   bool empty = false;
   if (check_common(B, H, N, d, 1.f, causal, &empty) != FA_OK) return 0;
   if (empty) return 0;
-  const size_t delta = (size_t)B * H * N * sizeof(float);
-  return (delta + 255) & ~(size_t)255;
+  const size_t bytes = 2 * (size_t)B * H * N * sizeof(float);  // D and L log2(e)
+  return (bytes + 255) & ~(size_t)255;
 }
 
-int fa_bwd_preprocess(const void* o, const void* dO, float* delta, int B, int H, int N, int d,
-                      void* stream) {
+int fa_bwd_preprocess(const void* o, const void* dO, const float* lse, void* workspace,
+                      size_t workspace_bytes, int B, int H, int N, int d, void* stream) {
   bool empty = false;
   int st = check_common(B, H, N, d, 1.f, 0, &empty);
   if (st != FA_OK || empty) return st;
-  if (!o || !dO || !delta) return FA_ERR_INVALID_ARG;
-  if (!aligned16(o) || !aligned16(dO) || !aligned16(delta)) return FA_ERR_UNSUPPORTED;
-  hipError_t e = fa::launch_bwd_pre(o, dO, delta, B, H, N, static_cast<hipStream_t>(stream));
+  if (!o || !dO || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(o) || !aligned16(dO) || !aligned16(lse)) return FA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, H, N, d, 0) || !aligned16(workspace))
+    return FA_ERR_WORKSPACE;
+  hipError_t e = fa::launch_bwd_pre(o, dO, lse, static_cast<float*>(workspace), B, H, N,
+                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                const float* delta, void* dk, void* dv, int B, int H, int N, int d, float scale,
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
+                size_t workspace_bytes, void* dk, void* dv, int B, int H, int N, int d, float scale,
                 int causal, void* stream) {
   bool empty = false;
   int st = check_common(B, H, N, d, scale, causal, &empty);
   if (st != FA_OK || empty) return st;
-  if (!q || !k || !v || !dO || !lse || !delta || !dk || !dv) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) ||
-      !aligned16(delta) || !aligned16(dk) || !aligned16(dv))
+  if (!q || !k || !v || !dO || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(dk) ||
+      !aligned16(dv))
     return FA_ERR_UNSUPPORTED;
-  hipError_t e = fa::launch_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, B, H, N, scale, causal,
-                                     static_cast<hipStream_t>(stream));
+  if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, H, N, d, causal) ||
+      !aligned16(workspace))
+    return FA_ERR_WORKSPACE;
+  hipError_t e = fa::launch_bwd_dkdv(q, k, v, dO, static_cast<const float*>(workspace), dk, dv, B,
+                                     H, N, scale, causal, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-              const float* delta, void* dq, int B, int H, int N, int d, float scale, int causal,
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
+              size_t workspace_bytes, void* dq, int B, int H, int N, int d, float scale, int causal,
               void* stream) {
   bool empty = false;
   int st = check_common(B, H, N, d, scale, causal, &empty);
   if (st != FA_OK || empty) return st;
-  if (!q || !k || !v || !dO || !lse || !delta || !dq) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(lse) ||
-      !aligned16(delta) || !aligned16(dq))
+  if (!q || !k || !v || !dO || !dq) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(dq))
     return FA_ERR_UNSUPPORTED;
-  hipError_t e = fa::launch_bwd_dq(q, k, v, dO, lse, delta, dq, B, H, N, scale, causal,
-                                   static_cast<hipStream_t>(stream));
+  if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, H, N, d, causal) ||
+      !aligned16(workspace))
+    return FA_ERR_WORKSPACE;
+  hipError_t e = fa::launch_bwd_dq(q, k, v, dO, static_cast<const float*>(workspace), dq, B, H, N,
+                                   scale, causal, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -108,12 +116,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     return FA_ERR_UNSUPPORTED;
   const size_t need = fa_bwd_workspace_size(B, H, N, d, causal);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
-  float* delta = static_cast<float*>(workspace);
+  float* ws = static_cast<float*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = fa::launch_bwd_pre(o, dO, delta, B, H, N, s);
-  if (e == hipSuccess)
-    e = fa::launch_bwd_dkdv(q, k, v, dO, lse, delta, dk, dv, B, H, N, scale, causal, s);
-  if (e == hipSuccess) e = fa::launch_bwd_dq(q, k, v, dO, lse, delta, dq, B, H, N, scale, causal, s);
+  hipError_t e = fa::launch_bwd_pre(o, dO, lse, ws, B, H, N, s);
+  if (e == hipSuccess) e = fa::launch_bwd_dkdv(q, k, v, dO, ws, dk, dv, B, H, N, scale, causal, s);
+  if (e == hipSuccess) e = fa::launch_bwd_dq(q, k, v, dO, ws, dq, B, H, N, scale, causal, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

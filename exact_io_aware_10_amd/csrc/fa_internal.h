@@ -10,16 +10,16 @@ namespace fa {
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int H, int N, float scale, int causal, hipStream_t stream);
 
-// D = rowsum(dO * O), B*H*N floats.
-hipError_t launch_bwd_pre(const void* o, const void* dO, float* delta, int B, int H, int N,
-                          hipStream_t stream);
+// Backward workspace layout (2 B*H*N floats): [D = rowsum(dO * O) | L * log2(e)].
+hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* ws, int B, int H,
+                          int N, hipStream_t stream);
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
-                           const float* lse, const float* delta, void* dk, void* dv, int B, int H,
-                           int N, float scale, int causal, hipStream_t stream);
+                           const float* ws, void* dk, void* dv, int B, int H, int N, float scale,
+                           int causal, hipStream_t stream);
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
-                         const float* lse, const float* delta, void* dq, int B, int H, int N,
-                         float scale, int causal, hipStream_t stream);
+                         const float* ws, void* dq, int B, int H, int N, float scale, int causal,
+                         hipStream_t stream);
 
 }  // namespace fa

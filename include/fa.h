@@ -63,8 +63,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes (at least B*H*N
- * float32 for D = rowsum(dO * O)).  Returns 0 when the sizes are invalid.
+ * Bytes of device workspace the backward pass needs for these sizes:
+ * 2*B*H*N float32 (rounded up to 256 bytes), laid out as [D | L*log2(e)],
+ * with D_i = sum_k dO_ik O_ik and L the forward's log-sum-exp.  Returns 0
+ * when the sizes are invalid or empty.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal);
 
@@ -75,12 +77,13 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal);
  *   dq, dk, dv     : [B,H,N,d] bf16 outputs.
  *   workspace      : device buffer of at least fa_bwd_workspace_size() bytes,
  *                    16-byte aligned; its contents on entry are ignored and
- *                    on exit are unspecified.
+ *                    on exit hold [D | L*log2(e)].
  * P is recomputed tile by tile as exp(scale q.k - L_i); with
  * dP = dO V^T and D_i = sum_k dO_ik O_ik, dS = P o (dP - D), and
  * dV = P^T dO, dQ = scale dS K, dK = scale dS^T Q ("Interrogating the GPU,
  * part 5", section "What does the backward pass do without P?"; dQ and dK
- * by the chain rule).
+ * by the chain rule).  Deterministic: no atomics, so repeated calls give
+ * bitwise identical gradients.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
            const float* lse, void* dq, void* dk, void* dv,
@@ -90,25 +93,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 /*
  * The three stages fa_bwd runs, in order, on one stream.  Each is exposed so a
  * caller can schedule or time them separately; running all three with the
- * same arguments is exactly fa_bwd.  Arguments as for fa_bwd; delta is a
- * device buffer of B*H*N float32 (16-byte aligned), written by
- * fa_bwd_preprocess and read by the other two.
+ * same arguments and workspace is exactly fa_bwd.  Arguments as for fa_bwd.
  *
- * fa_bwd_preprocess: delta_i = D_i = sum_k dO_ik O_ik, the row sum of dO o O
- *   that plays the role of delta in dS = P o (dP - delta) ("Interrogating
- *   the GPU, part 5", section "What does the backward pass do without P?").
+ * fa_bwd_preprocess: fills the workspace with D_i = sum_k dO_ik O_ik, the row
+ *   sum of dO o O that plays the role of delta in dS = P o (dP - delta)
+ *   ("Interrogating the GPU, part 5", section "What does the backward pass do
+ *   without P?"), and with L_i log2(e) for the exp2-based recomputation.
  * fa_bwd_dkdv: for each key block, recompute P = exp(scale q.k - L) over all
  *   visible queries and accumulate dV = P^T dO and dK = scale dS^T Q.
  * fa_bwd_dq: for each query block, recompute P and dS over all visible keys
  *   and accumulate dQ = scale dS K.
+ * The last two read the workspace the first one wrote.
  */
-int fa_bwd_preprocess(const void* o, const void* dO, float* delta,
+int fa_bwd_preprocess(const void* o, const void* dO, const float* lse,
+                      void* workspace, size_t workspace_bytes,
                       int B, int H, int N, int d, void* stream);
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
-                const float* lse, const float* delta, void* dk, void* dv,
+                const void* workspace, size_t workspace_bytes, void* dk, void* dv,
                 int B, int H, int N, int d, float scale, int causal, void* stream);
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
-              const float* lse, const float* delta, void* dq,
+              const void* workspace, size_t workspace_bytes, void* dq,
               int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /* Static, human-readable text for a status code (never NULL). */
