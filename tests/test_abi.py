@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every entry point include/fa.h declares,
+and rejects bad arguments before touching the GPU (no compute call here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import exact_io_aware_10_amd as fa  # imports torch first: one HIP runtime per process
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.skip("libfa.so not built")
+    fa.load_library()
+    return fa
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    for n in ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_strerror", "fa_bwd_preprocess",
+              "fa_bwd_dkdv", "fa_bwd_dq"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(fa):
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    for n in declared():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(fa):
+    for st in range(5):
+        assert fa.fa_strerror(st)
+    assert "unknown" in fa.fa_strerror(99)
+
+
+def test_workspace_size(fa):
+    assert fa.fa_bwd_workspace_size(1, 64, 8192, 128, True) == 2 * 64 * 8192 * 4
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 128, False) == 256
+    assert fa.fa_bwd_workspace_size(1, 1, 3, 64, False) == 0
+    assert fa.fa_bwd_workspace_size(-1, 1, 3, 128, False) == 0
+    assert fa.fa_bwd_workspace_size(0, 1, 3, 128, False) == 0
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("args,expect", [
+    # (B, H, N, d, scale, causal, misalign q) -> status
+    ((1, 1, 16, 64, 0.1, 0, 0), 2),
+    ((1, 1, 16, 128, float("nan"), 0, 0), 1),
+    ((1, 1, 16, 128, float("inf"), 0, 0), 1),
+    ((1, 1, 16, 128, 0.0, 0, 0), 1),
+    ((1, 1, 16, 128, -0.5, 0, 0), 1),
+    ((1, 1, 16, 128, 0.1, 2, 0), 1),
+    ((-1, 1, 16, 128, 0.1, 0, 0), 1),
+    ((1, -1, 16, 128, 0.1, 0, 0), 1),
+    ((1, 1, -16, 128, 0.1, 0, 0), 1),
+    ((1, 1, 16, 128, 0.1, 0, 8), 2),
+    ((64, 64, 4096, 128, 0.1, 0, 0), 2),  # B*H*N*d = 2^31: index overflow guard
+])
+def test_fwd_rejects_bad_arguments(fa, args, expect):
+    B, H, N, d, scale, causal, mis = args
+    lib = fa.load_library()
+    assert lib.fa_fwd(FAKE + mis, FAKE, FAKE, FAKE, FAKE, B, H, N, d, scale, causal, None) == expect
+
+
+def test_fwd_rejects_null_pointers(fa):
+    lib = fa.load_library()
+    for i in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[i] = None
+        assert lib.fa_fwd(*ptrs, 1, 1, 16, 128, 0.1, 0, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_empty_problem_is_a_no_op(fa):
+    lib = fa.load_library()
+    assert lib.fa_fwd(None, None, None, None, None, 0, 4, 16, 128, 0.1, 0, None) == fa.FA_OK
+    assert lib.fa_fwd(None, None, None, None, None, 1, 1, 0, 128, 0.1, 1, None) == fa.FA_OK
+    assert lib.fa_bwd(*([None] * 9), 1, 0, 16, 128, 0.1, 0, None, 0, None) == fa.FA_OK
+
+
+def test_bwd_rejects_bad_workspace(fa):
+    lib = fa.load_library()
+    p = [FAKE] * 9
+    assert lib.fa_bwd(*p, 1, 1, 16, 128, 0.1, 1, None, 1 << 20, None) == fa.FA_ERR_WORKSPACE
+    assert lib.fa_bwd(*p, 1, 1, 16, 128, 0.1, 1, FAKE, 16, None) == fa.FA_ERR_WORKSPACE
+    assert lib.fa_bwd(*p, 1, 1, 16, 128, 0.1, 1, FAKE + 4, 1 << 20, None) == fa.FA_ERR_WORKSPACE
+    assert lib.fa_bwd_preprocess(FAKE, FAKE, FAKE, FAKE, 8, 1, 1, 16, 128, None) == fa.FA_ERR_WORKSPACE
+    assert lib.fa_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, 1, 1, 16, 128, 0.1, 0, None) == fa.FA_ERR_WORKSPACE
+    assert lib.fa_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 1, 1, 16, 128, 0.1, 0, None) == fa.FA_ERR_WORKSPACE
+
+
+def test_bwd_rejects_bad_shapes(fa):
+    lib = fa.load_library()
+    p = [FAKE] * 9
+    assert lib.fa_bwd(*p, 1, 1, 16, 96, 0.1, 0, FAKE, 1 << 20, None) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_bwd(*p, 1, 1, 16, 128, float("nan"), 0, FAKE, 1 << 20, None) == fa.FA_ERR_INVALID_ARG
+    p[3] = None
+    assert lib.fa_bwd(*p, 1, 1, 16, 128, 0.1, 0, FAKE, 1 << 20, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_binding_requires_device_tensors(fa):
+    import torch
+    t = torch.zeros((1, 1, 4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(t, t, t, 0.1, False)
