@@ -102,9 +102,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int col = lane & 31;
 
   // Causal: the first key blocks see the most queries; issue them first.
-  const int id = blockIdx.x;
-  const int kb = id / BH;
-  const int bh = id % BH;
+  int kb, bh;
+  block_head(blockIdx.x, (N + KV_BK - 1) / KV_BK, BH, false, &kb, &bh);
   const int k0 = kb * KV_BK;
   const int kw = k0 + kg * 32;
   const int krow = kw + col;
@@ -298,9 +297,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int h = lane >> 5;
   const int col = lane & 31;
 
-  const int id = blockIdx.x;
-  const int qblk = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
-  const int bh = id % BH;
+  int qblk, bh;
+  block_head(blockIdx.x, nqb, BH, CAUSAL, &qblk, &bh);
   const int q0 = qblk * DQ_BQ;
   const int q0w = q0 + wave * 32;
   const int qrow = q0w + col;

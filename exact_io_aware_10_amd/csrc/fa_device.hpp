@@ -39,14 +39,14 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 // Physical 16-byte chunk of logical chunk c (0..15) in tile row r.  The map
-// is c ^ f(r) with f a bit permutation of r & 15 (bits b3 b2 b1 b0 ->
-// b3 b1 b0 b2), so
+// is c ^ f(r) with f swapping the two 2-bit halves of r & 15, so
 //   * 16 consecutive rows reading one logical chunk hit 16 distinct chunks
-//     (row-wise MFMA operand reads), and
-//   * 4 consecutive rows (aligned to 4) reading two adjacent logical chunks
-//     hit 8 distinct chunks (the transpose reads).
+//     (row-wise MFMA operand reads, ds_read_b128), and
+//   * 4 consecutive rows (aligned to 4) reading 4 adjacent logical chunks
+//     (aligned to 4) hit 16 distinct chunks: the 32 lanes of a transpose read
+//     (ds_read_b64_tr_b16) cover all 64 banks.
 __device__ __forceinline__ int swz(int r) {
-  return (r & 8) | ((r & 3) << 1) | ((r >> 2) & 1);
+  return ((r & 3) << 2) | ((r >> 2) & 3);
 }
 __device__ __forceinline__ int tile_off(int row, int chunk) {
   return row * kRowBytes + ((chunk ^ swz(row)) << 4);
@@ -90,10 +90,13 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Round-to-nearest-even float -> bf16 pair (v_cvt_pk_bf16_f32 on gfx950).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even float pair -> packed bf16 pair (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5,
@@ -113,10 +116,33 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }
 // 16 bytes per lane from global memory straight into LDS: lane i writes
-// lds_base + 16 i (lds_base must be wave-uniform).
-__device__ __forceinline__ void buf_load16_lds(rsrc_t r, char* lds_base, uint32_t voff) {
+// lds_base + 16 i (lds_base must be wave-uniform).  The global byte offset is
+// voff (per lane) + soff (wave-uniform).
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, char* lds_base, uint32_t voff,
+                                               uint32_t soff = 0) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
-                                           voff, 0, 0, 0);
+                                           voff, soff, 0, 0);
+}
+
+// Workgroup -> (block, head) map.  Workgroups are dealt round-robin to the 8
+// XCDs (each with its own L2), so when the head count is a multiple of 8 the
+// blocks of one head are given to one XCD and issued together there: the
+// head's K/V (or Q/dO) stream is then shared through that XCD's L2.  Within a
+// head, blocks go in the order `rev` asks for (longest causal work first).
+constexpr int kXcds = 8;
+__device__ __forceinline__ void block_head(int id, int nblk, int BH, bool rev, int* blk, int* bh) {
+  int b, hd;
+  if ((BH % kXcds) == 0) {
+    const int xcd = id % kXcds;
+    const int local = id / kXcds;
+    hd = xcd + kXcds * (local / nblk);
+    b = local % nblk;
+  } else {
+    hd = id % BH;
+    b = id / BH;
+  }
+  *blk = rev ? (nblk - 1 - b) : b;
+  *bh = hd;
 }
 
 __device__ __forceinline__ u32x4 load16_or_zero(const char* p, bool ok) {

@@ -21,6 +21,8 @@
 // tiles wholly after a wave's last query are skipped by that wave, and the
 // diagonal tiles are masked element-wise ("LLM flash attention", section
 // "End-to-end flow").
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -41,13 +43,19 @@ constexpr int FWD_LOADS = FWD_TILE / 1024 / FWD_WAVES;  // 1 KiB LDS-direct load
 // reference maximum that LSE records).
 constexpr float kTau = 8.f;
 
+template <int V>
+using ic = std::integral_constant<int, V>;
+
 template <bool CAUSAL>
 __global__ __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                 float* __restrict__ lse, int BH, int N, int nqb, float sl2) {
   // [buffer][K | V] tiles, each 64 rows x 256 bytes, swizzled (tile_off).
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * FWD_TILE];
+  __shared__ __attribute__((aligned(16))) char k_lds0[FWD_TILE];
+  __shared__ __attribute__((aligned(16))) char k_lds1[FWD_TILE];
+  __shared__ __attribute__((aligned(16))) char v_lds0[FWD_TILE];
+  __shared__ __attribute__((aligned(16))) char v_lds1[FWD_TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -55,11 +63,9 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int h = lane >> 5;
   const int col = lane & 31;
 
-  // Causal: issue the longest query blocks first.  Consecutive workgroups
-  // take consecutive heads of one query block.
-  const int id = blockIdx.x;
-  const int qb = CAUSAL ? (nqb - 1 - id / BH) : (id / BH);
-  const int bh = id % BH;
+  // Causal: issue the longest query blocks first.
+  int qb, bh;
+  block_head(blockIdx.x, nqb, BH, CAUSAL, &qb, &bh);
   const int q0 = qb * FWD_BR;
   const int q0w = q0 + wave * FWD_QW;
   const int qrow = q0w + col;
@@ -82,24 +88,44 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // Tile loader: LDS-direct buffer loads.  Instruction n of wave w fills rows
   // 16 n + 4 w .. + 3 (1 KiB, lane-linear in LDS); lane i lands on physical
   // chunk i % 16 of its row and so fetches the logical chunk stored there.
-  const int ld_sub = lane >> 4;
-  const int ld_pc = lane & 15;
-  auto issue_tile = [&](int t, int buf) {
-    char* kb = smem + buf * 2 * FWD_TILE;
-    char* vb = kb + FWD_TILE;
+  // The tile's row offset goes in the wave-uniform soffset.
+  uint32_t ld_voff[FWD_LOADS];
+#pragma unroll
+  for (int n = 0; n < FWD_LOADS; ++n) {
+    const int row = 16 * n + 4 * wave + (lane >> 4);
+    ld_voff[n] = (uint32_t)row * kRowBytes + (((lane & 15) ^ swz(row)) << 4);
+  }
+  auto issue_tile = [&](int t, auto bufc) {
+    char* kb = decltype(bufc)::value ? k_lds1 : k_lds0;
+    char* vb = decltype(bufc)::value ? v_lds1 : v_lds0;
+    const uint32_t soff = (uint32_t)t * FWD_TILE;
 #pragma unroll
     for (int n = 0; n < FWD_LOADS; ++n) {
       const int row0 = 16 * n + 4 * wave;
-      const int row = row0 + ld_sub;
-      const uint32_t voff = (uint32_t)(t * FWD_BC + row) * kRowBytes + ((ld_pc ^ swz(row)) << 4);
-      buf_load16_lds(rk, kb + row0 * kRowBytes, voff);
-      buf_load16_lds(rv, vb + row0 * kRowBytes, voff);
+      buf_load16_lds(rk, kb + row0 * kRowBytes, ld_voff[n], soff);
+      buf_load16_lds(rv, vb + row0 * kRowBytes, ld_voff[n], soff);
     }
   };
 
-  issue_tile(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // Per-lane LDS offsets, fixed for the whole kernel (tile-relative):
+  //   K rows for S^T: row col (+ 32 st), logical chunk 2 kc + h;
+  //   V transpose reads: row 4 h + (lane % 16) / 4 (+ 8, + 16 u, + 32 st),
+  //   dims 32 mb + 16 ((lane / 16) % 2) + 4 (lane % 4).
+  int koff[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) koff[kc] = tile_off(col, 2 * kc + h);
+  int voff[4][2];
+  {
+    const int tr_s = lane & 15;
+    const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (tr_s & 3);
+    const int tr_row = 4 * h + (tr_s >> 2);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int dim = 32 * mb + tr_dim;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) voff[mb][e] = tile_off8(tr_row + 8 * e, dim >> 3, (dim >> 2) & 1);
+    }
+  }
 
   f32x16 acc[4];
 #pragma unroll
@@ -109,19 +135,14 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   float m = -INFINITY;  // reference maximum, log2 domain of the scaled scores
   float l = 0.f;        // running sum over this lane's half of each tile
 
-  // Transpose-read addressing for V (see lds_read_tr): 16-lane group of dims.
-  const int tr_s = lane & 15;
-  const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (tr_s & 3);  // + 32 mb
-  const int tr_row = 4 * h + (tr_s >> 2);                      // + 32 st + 16 u (+ 8)
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
+  auto step = [&](int t, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    if (t + 1 < ntiles) issue_tile(t + 1, ic<BUF ^ 1>{});
     const int k0 = t * FWD_BC;
     const bool active = !CAUSAL || (k0 <= q0w + FWD_QW - 1);
     if (active) {
-      const char* kb = smem + buf * 2 * FWD_TILE;
-      const char* vb = kb + FWD_TILE;
+      const char* kb = BUF ? k_lds1 : k_lds0;
+      const char* vb = BUF ? v_lds1 : v_lds0;
 
       f32x16 s[2];
 #pragma unroll
@@ -130,7 +151,7 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
 #pragma unroll
         for (int kc = 0; kc < 8; ++kc) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, lds_read16(kb, tile_off(32 * st + col, 2 * kc + h)));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, lds_read16(kb + st * 32 * kRowBytes, koff[kc]));
           s[st] = mfma32(a, qf[kc], s[st]);
         }
       }
@@ -188,22 +209,27 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const int dim = 32 * mb + tr_dim;
-        const int chunk = dim >> 3;
-        const int half = (dim >> 2) & 1;
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            const int r = 32 * st + 16 * u + tr_row;
-            const i16x4 lo = lds_read_tr(vb + tile_off8(r, chunk, half));
-            const i16x4 hi = lds_read_tr(vb + tile_off8(r + 8, chunk, half));
+            const char* rb = vb + (32 * st + 16 * u) * kRowBytes;
+            const i16x4 lo = lds_read_tr(rb + voff[mb][0]);
+            const i16x4 hi = lds_read_tr(rb + voff[mb][1]);
             acc[mb] = mfma32(join(lo, hi), pb[st][u], acc[mb]);
           }
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+
+  issue_tile(0, ic<0>{});
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, ic<0>{});
+    if (t + 1 < ntiles) step(t + 1, ic<1>{});
   }
 
   const float lt = halves_sum(l);
