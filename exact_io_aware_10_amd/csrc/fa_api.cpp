@@ -27,6 +27,9 @@ int check_common(int B, int H, int N, int d, float scale, int causal, bool* empt
   }
   const int64_t elems = (int64_t)B * H * N * d;
   if (elems >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
+  // Per-head byte offsets (plus one tile of padding) must fit the 32-bit
+  // buffer offsets the kernels use.
+  if ((int64_t)N * d * 2 + 65536 >= ((int64_t)1 << 32)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

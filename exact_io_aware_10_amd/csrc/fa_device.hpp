@@ -116,12 +116,11 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }
 // 16 bytes per lane from global memory straight into LDS: lane i writes
-// lds_base + 16 i (lds_base must be wave-uniform).  The global byte offset is
-// voff (per lane) + soff (wave-uniform).
-__device__ __forceinline__ void buf_load16_lds(rsrc_t r, char* lds_base, uint32_t voff,
-                                               uint32_t soff = 0) {
+// lds_base + 16 i (lds_base must be wave-uniform).  The global byte offset
+// voff is per lane and is the part the hardware range-checks.
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, char* lds_base, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
-                                           voff, soff, 0, 0);
+                                           voff, 0, 0, 0);
 }
 
 // Workgroup -> (block, head) map.  Workgroups are dealt round-robin to the 8

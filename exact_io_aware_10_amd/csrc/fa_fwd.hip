@@ -88,7 +88,8 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // Tile loader: LDS-direct buffer loads.  Instruction n of wave w fills rows
   // 16 n + 4 w .. + 3 (1 KiB, lane-linear in LDS); lane i lands on physical
   // chunk i % 16 of its row and so fetches the logical chunk stored there.
-  // The tile's row offset goes in the wave-uniform soffset.
+  // The tile's row offset is added to the per-lane offset, the part the
+  // hardware range-checks, so rows past N read as zero.
   uint32_t ld_voff[FWD_LOADS];
 #pragma unroll
   for (int n = 0; n < FWD_LOADS; ++n) {
@@ -98,12 +99,12 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   auto issue_tile = [&](int t, auto bufc) {
     char* kb = decltype(bufc)::value ? k_lds1 : k_lds0;
     char* vb = decltype(bufc)::value ? v_lds1 : v_lds0;
-    const uint32_t soff = (uint32_t)t * FWD_TILE;
+    const uint32_t toff = (uint32_t)t * FWD_TILE;
 #pragma unroll
     for (int n = 0; n < FWD_LOADS; ++n) {
       const int row0 = 16 * n + 4 * wave;
-      buf_load16_lds(rk, kb + row0 * kRowBytes, ld_voff[n], soff);
-      buf_load16_lds(rv, vb + row0 * kRowBytes, ld_voff[n], soff);
+      buf_load16_lds(rk, kb + row0 * kRowBytes, ld_voff[n] + toff);
+      buf_load16_lds(rv, vb + row0 * kRowBytes, ld_voff[n] + toff);
     }
   };
 
@@ -146,15 +147,23 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
       f32x16 s[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
 #pragma unroll
-        for (int kc = 0; kc < 8; ++kc) {
+      for (int kc = 0; kc < 8; ++kc)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
           const bf16x8 a = __builtin_bit_cast(bf16x8, lds_read16(kb + st * 32 * kRowBytes, koff[kc]));
           s[st] = mfma32(a, qf[kc], s[st]);
         }
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < 10; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
 
       const bool need_mask = (CAUSAL && (k0 + FWD_BC - 1 > q0w)) || (k0 + FWD_BC > N);
       if (need_mask) {
@@ -208,17 +217,16 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
 
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
+          for (int mb = 0; mb < 4; ++mb) {
             const char* rb = vb + (32 * st + 16 * u) * kRowBytes;
             const i16x4 lo = lds_read_tr(rb + voff[mb][0]);
             const i16x4 hi = lds_read_tr(rb + voff[mb][1]);
             acc[mb] = mfma32(join(lo, hi), pb[st][u], acc[mb]);
           }
-      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

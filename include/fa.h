@@ -18,7 +18,8 @@
  *   - Layout: contiguous row-major [B, H, N, d] for q, k, v, o, dO, dq, dk,
  *     dv (bfloat16, 2 bytes per element); contiguous [B, H, N] float32 for
  *     lse.  Base pointers must be 16-byte aligned.
- *   - d must be 128.  B, H, N >= 0 and B*H*N*d below 2^31; when any of B,
+ *   - d must be 128.  B, H, N >= 0, B*H*N*d below 2^31 and N below 2^24 - 256;
+ *     when any of B,
  *     H, N is 0 there is nothing to compute and the call returns FA_OK
  *     without touching any pointer.
  *   - scale must be finite and > 0 (the scores are scale * q . k).

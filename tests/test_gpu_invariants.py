@@ -221,3 +221,39 @@ def test_error_paths_with_device_tensors(fa):
     # Empty problem: nothing launched, success.
     assert lib.fa_fwd(None, None, None, None, None, 1, 1, 0, 128, SCALE, 0, None) == fa.FA_OK
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [100, 1000])
+def test_tail_reads_stay_inside_each_head(fa, causal, N):
+    """Rows past N of a head must read as zero, never as the next head's rows
+    or memory past the tensor: fill head 1 and a tail guard band with NaN and
+    check that head 0 (forward and backward) is finite and matches the same
+    problem run on its own."""
+    import torch
+    x = fa_inputs.make(1, 1, N, seed=9970 + N, with_do=True)
+    nan = torch.tensor(float("nan"), dtype=torch.bfloat16)
+    t = {}
+    for nm in ("q", "k", "v", "do"):
+        buf = torch.full((1, 3, N, 128), nan, dtype=torch.bfloat16, device="cuda")
+        buf[:, 0] = to_dev(x[nm], torch)[:, 0]
+        t[nm] = buf[:, :2]  # head 1 and the third (guard) head hold NaN
+    # Views of the first two heads of 3-head buffers: contiguous, with a NaN
+    # guard head right after them in memory.
+    q2, k2, v2, do2 = (t[nm] for nm in ("q", "k", "v", "do"))
+    assert q2.is_contiguous()
+    o2, l2 = fa.forward(q2, k2, v2, SCALE, causal)
+    q1, k1, v1, do1 = (to_dev(x[nm], torch) for nm in ("q", "k", "v", "do"))
+    o1, l1 = fa.forward(q1, k1, v1, SCALE, causal)
+    g1 = fa.backward(q1, k1, v1, o1, do1, l1, SCALE, causal)
+    o2h = o2[:, :1].contiguous()
+    l2h = l2[:, :1].contiguous()
+    torch.cuda.synchronize()
+    assert torch.equal(o2h, o1) and torch.equal(l2h, l1)
+    # backward of head 0 with NaN neighbours: only head 0's rows are inputs to it
+    o2[:, 1] = 0
+    l2[:, 1] = 0
+    g2 = fa.backward(q2, k2, v2, o2, do2, l2, SCALE, causal)
+    torch.cuda.synchronize()
+    for a, b in zip(g2, g1):
+        assert torch.equal(a[:, :1].contiguous(), b)
