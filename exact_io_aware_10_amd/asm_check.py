@@ -1,0 +1,86 @@
+"""Build-time check of the kernels' inline-assembly MFMAs.
+
+Some MFMAs in the kernels are written as inline assembly (accumulators kept
+in VGPRs or AGPRs against the compiler's own choice).  The compiler's hazard
+recognizer does not look inside inline assembly, so nothing stops the
+register allocator from placing a copy of such an MFMA's result right after
+it, before the matrix core has written the result.  The kernels bracket those
+MFMAs with fences; this check verifies the generated code: no instruction may
+read or overwrite the destination registers of an inline-assembly MFMA within
+MIN_WAIT wait states of it (an 8-pass 32x32 MFMA needs about 11).
+
+Usage: python -m exact_io_aware_10_amd.asm_check FILE.s ...
+"""
+from __future__ import annotations
+
+import re
+import sys
+
+MIN_WAIT = 12
+
+_RANGE = re.compile(r"([av])\[(\d+):(\d+)\]")
+_SINGLE = re.compile(r"([av])(\d+)$")
+
+
+def _regs(tok: str) -> set:
+    m = _RANGE.fullmatch(tok)
+    if m:
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = _SINGLE.fullmatch(tok)
+    if m:
+        return {(m.group(1), int(m.group(2)))}
+    return set()
+
+
+def _parse(text: str):
+    insts, in_asm = [], False
+    for ln, line in enumerate(text.split("\n"), 1):
+        if ";;#ASMSTART" in line:
+            in_asm = True
+        elif ";;#ASMEND" in line:
+            in_asm = False
+        body = line.split(";")[0].strip()
+        if not body or body.startswith(".") or body.endswith(":"):
+            continue
+        parts = body.replace(",", " ").split()
+        insts.append((ln, parts[0], parts[1:], in_asm))
+    return insts
+
+
+def check(text: str, min_wait: int = MIN_WAIT) -> list[str]:
+    """Return one message per early access to an inline-asm MFMA result."""
+    insts = _parse(text)
+    problems = []
+    for idx, (ln, op, ops, in_asm) in enumerate(insts):
+        if not (in_asm and op.startswith("v_mfma")):
+            continue
+        dst = _regs(ops[0])
+        waited = 0
+        for ln2, op2, ops2, _ in insts[idx + 1:]:
+            waited += int(ops2[0], 0) + 1 if op2 == "s_nop" else 1
+            if waited > min_wait or op2.startswith(("s_branch", "s_cbranch", "s_endpgm", "s_setpc")):
+                break
+            touched = set()
+            for tok in ops2:
+                touched |= _regs(tok)
+            if op2.startswith("v_mfma") and _regs(ops2[0]) == dst and ops2[3:4] == [ops[0]]:
+                continue  # accumulation chain into the same registers: forwarded
+            if dst & touched:
+                problems.append(f"line {ln}: {op} {ops[0]} is accessed {waited} wait states "
+                                f"later at line {ln2}: {op2} {' '.join(ops2)}")
+                break
+    return problems
+
+
+def main(argv: list[str]) -> int:
+    bad = 0
+    for path in argv:
+        with open(path) as f:
+            for msg in check(f.read()):
+                print(f"{path}: {msg}")
+                bad += 1
+    return 1 if bad else 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))

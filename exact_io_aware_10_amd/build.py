@@ -34,7 +34,25 @@ def _compile(src: str) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    if src.endswith(".hip"):
+        _check_asm(src)
     return obj
+
+
+def _check_asm(src: str) -> None:
+    """Verify the inline-assembly MFMAs of one source in its generated code."""
+    from . import asm_check
+
+    asm = os.path.join(BUILD, os.path.basename(src) + ".s")
+    cmd = [HIPCC, *COMMON, "-x", "hip", "--cuda-device-only", "-S", os.path.join(CSRC, src),
+           "-o", asm]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
+    with open(asm) as f:
+        problems = asm_check.check(f.read())
+    if problems:
+        raise RuntimeError(f"{src}: inline-asm MFMA results read too early:\n" + "\n".join(problems))
 
 
 def build(verbose: bool = False) -> str:

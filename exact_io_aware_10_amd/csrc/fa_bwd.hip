@@ -11,7 +11,7 @@
 //
 // Three launches, no atomics (bitwise deterministic):
 //   bwd_pre   workspace <- [D = rowsum(dO o O) | L log2(e)]   HBM-bound
-//   bwd_dkdv  per key block: K, V held in registers; query tiles of Q, dO,
+//   bwd_dkdv  per key block: K in registers, V in LDS; query tiles of Q, dO,
 //             L log2(e), D stream through LDS; dV^T += dO^T P, dK^T += Q^T dS
 //   bwd_dq    per query block: Q, dO, L, D held in registers; K, V tiles
 //             stream through LDS; dQ^T += K^T dS^T
@@ -26,10 +26,55 @@ namespace fa {
 __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
 }
-// 4 bytes per lane straight into LDS: lane i writes lds_base + 4 i.
-__device__ __forceinline__ void buf_load4_lds(rsrc_t r, char* lds_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4,
-                                           voff, 0, 0, 0);
+
+// LDS-direct loads written as inline assembly, invisible to the compiler's
+// LDS dependency tracking: kernels that use them order the ring themselves
+// (ring_wait_barrier).  M0 carries the wave-uniform LDS base; nothing else in
+// these kernels uses M0.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+// lds_base: wave-uniform LDS byte address (lds_addr of the destination);
+// 16 (dma16) or 4 (dma4) bytes per lane, lane i writing lds_base + size i.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(r)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(r)
+               : "memory");
+}
+// Wait until at most PENDING of this wave's LDS-direct loads are in flight
+// and its LDS reads are done, then barrier.  The "memory" clobber keeps the
+// compiler from moving LDS accesses across it.
+template <int PENDING>
+__device__ __forceinline__ void ring_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(PENDING) : "memory");
+}
+__device__ __forceinline__ void dma_drain() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
+
+// MFMA with the accumulator in VGPRs, as inline assembly.  In kernels that
+// run one wave per SIMD the compiler gives every MFMA an AGPR accumulator;
+// the score tiles S and dP are read by VALU code right after, so they are
+// kept in VGPRs this way.  Hazards the compiler does not see here:
+//   * operands written by VALU need 2 wait states before the MFMA reads them
+//     (the leading s_nop 1);
+//   * VALU access to the result needs the MFMA drained: mfma_v_fence below
+//     (16 wait states) sits between the last MFMA and the first such access.
+// Back-to-back accumulation into the same registers needs no wait states.
+__device__ __forceinline__ void mfma_v_init(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b) : "memory");
+}
+__device__ __forceinline__ void mfma_v(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b) : "memory");
+}
+__device__ __forceinline__ void mfma_v_fence(f32x16& c0, f32x16& c1, f32x16& c2, f32x16& c3) {
+  asm volatile("s_nop 15" : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
 }
 
 // ---------------------------------------------------------------------------
@@ -66,38 +111,57 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // ---------------------------------------------------------------------------
 // dK / dV
 //
-// A workgroup owns KV_BK = 128 keys of one head and runs 8 waves: wave w
-// holds keys 32 (w % 4) .. + 31 and the query half w / 4 of every streamed
-// 64-query tile, so the two waves of a key group split the queries and their
-// partial dK, dV are summed through LDS at the end.  K and V of the block sit
-// in LDS for the whole kernel; this keeps a wave at about 200 registers, two
-// waves per SIMD, so one wave's softmax arithmetic overlaps the other's MFMA.
+// One wave per SIMD, four waves per workgroup: wave w owns keys
+// k0 + 64 w .. + 63 as two groups of 32.  Its K fragments stay in registers
+// for the whole kernel and the workgroup's V block sits in LDS; 32-query
+// tiles of Q, dO, L log2(e) and D stream through a four-slot LDS ring.
+// Owning 64 keys lets each Q / dO fragment read from LDS feed two MFMAs.
+// The accumulators dK^T, dV^T (256 registers) live in AGPRs; S and dP are
+// computed by VGPR-accumulator MFMAs (mfma_v) so that the softmax can read
+// them directly.
 // ---------------------------------------------------------------------------
-constexpr int KV_BK = 128;                  // keys per workgroup
-constexpr int KV_WAVES = 8;
-constexpr int KV_BQ = 64;                   // queries per streamed tile
-constexpr int KV_TILE = KV_BQ * kRowBytes;  // 16 KiB (Q or dO)
-constexpr int KV_BLOCK = KV_BK * kRowBytes;  // 32 KiB (K or V block)
-constexpr int KV_STAGE = 2 * KV_TILE + 2 * KV_BQ * 4;  // Q, dO, L log2(e), D
-constexpr int KV_SMEM = 2 * KV_BLOCK + 2 * KV_STAGE;   // 130 KiB
+constexpr int KV_BK = 256;                   // keys per workgroup
+constexpr int KV_WAVES = 4;                  // 64 keys per wave
+constexpr int KV_BQ = 32;                    // queries per streamed tile
+constexpr int KV_TILE = KV_BQ * kRowBytes;   // 8 KiB (Q or dO)
+constexpr int KV_VBLK = KV_BK * kRowBytes;   // 64 KiB
 constexpr int KV_THREADS = KV_WAVES * 64;
+constexpr int KV_TLOADS = KV_TILE / 1024 / KV_WAVES;  // LDS-direct loads per wave per tensor
+constexpr int KV_VLOADS = KV_VBLK / 1024 / KV_WAVES;
+// Ring slot: Q tile, dO tile, then four 64-entry float arrays (L log2(e), D,
+// and two sinks): the 4-byte LDS-direct load writes one entry per lane, and
+// every wave issues one so that all waves issue the same number of loads.
+constexpr int KV_SLOT = 2 * KV_TILE + 4 * 256;
+constexpr int KV_NSLOT = 4;
+constexpr int KV_LOADS_PER_TILE = 2 * KV_TLOADS + 1;
+static_assert(KV_LOADS_PER_TILE == 5, "the ring wait below counts 5 loads per tile");
+constexpr int KV_SMEM = KV_VBLK + KV_NSLOT * KV_SLOT;
+
+template <int V>
+struct kv_ic {
+  static constexpr int value = V;
+};
+
+// Hides x from loop-invariant code motion: an LDS address built from it
+// stays "register + constant offset" instead of one hoisted register each.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(KV_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(KV_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
                      const float* __restrict__ ws, uint16_t* __restrict__ dk,
                      uint16_t* __restrict__ dv, int BH, int N, float sl2, float scale) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* kblk = smem;
-  char* vblk = smem + KV_BLOCK;
-  char* stage0 = smem + 2 * KV_BLOCK;
+  __shared__ __attribute__((aligned(16))) char smem[KV_SMEM];
+  const uint32_t smem_lds = lds_addr(smem);  // LDS byte address of smem (wave-uniform)
+  constexpr int kRing = KV_VBLK;              // byte offset of the ring in smem
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int kg = wave & 3;   // key group of 32
-  const int qh = wave >> 2;  // query half of each tile
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
   const int col = lane & 31;
 
@@ -105,8 +169,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   int kb, bh;
   block_head(blockIdx.x, (N + KV_BK - 1) / KV_BK, BH, false, &kb, &bh);
   const int k0 = kb * KV_BK;
-  const int kw = k0 + kg * 32;
-  const int krow = kw + col;
+  const int kw = k0 + 64 * wave;
 
   const size_t head = (size_t)bh * (size_t)N * kD;
   const uint32_t head_bytes = (uint32_t)N * kRowBytes;
@@ -117,155 +180,298 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const size_t rows = (size_t)BH * N;
   const rsrc_t rD = make_rsrc(ws + (size_t)bh * N, (uint32_t)N * 4);
   const rsrc_t rL = make_rsrc(ws + rows + (size_t)bh * N, (uint32_t)N * 4);
+  const rsrc_t rLD = (wave & 1) ? rD : rL;
 
+  // V block: instruction n of wave w fills rows 16 n + 4 w .. + 3.
   const int ld_sub = lane >> 4;
   const int ld_pc = lane & 15;
-  // K and V of the block: 128 rows each, 4 one-KiB loads per wave per tensor.
 #pragma unroll
-  for (int n = 0; n < KV_BK / 32; ++n) {
-    const int row0 = 32 * n + 4 * wave;
+  for (int n = 0; n < KV_VLOADS; ++n) {
+    const int row0 = 16 * n + 4 * wave;
     const int row = row0 + ld_sub;
-    const uint32_t voff = (uint32_t)(k0 + row) * kRowBytes + ((ld_pc ^ swz(row)) << 4);
-    buf_load16_lds(rk, kblk + row0 * kRowBytes, voff);
-    buf_load16_lds(rv, vblk + row0 * kRowBytes, voff);
+    dma16(rv, smem_lds + row0 * kRowBytes, (uint32_t)(k0 + row) * kRowBytes + ((ld_pc ^ swz(row)) << 4));
   }
+  // K as the B operand of S = Q K^T: lane holds K[kw + 32 g + col][16 kc + 8 h .. + 7].
+  bf16x8 kf[2][8];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc)
+      kf[g][kc] = __builtin_bit_cast(
+          bf16x8, buf_load16(rk, (uint32_t)(kw + 32 * g + col) * kRowBytes + (2 * kc + h) * 16));
+  // Touch kf once here: the compiler waits for the loads at this point, and
+  // knows from then on that they have arrived.
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) asm volatile("" : : "v"(kf[g][kc]));
+
+  uint32_t ld_voff[KV_TLOADS];
+#pragma unroll
+  for (int n = 0; n < KV_TLOADS; ++n) {
+    const int row = 16 * n + 4 * wave + ld_sub;
+    ld_voff[n] = (uint32_t)row * kRowBytes + ((ld_pc ^ swz(row)) << 4);
+  }
+  // Loads of tile t into ring slot `sl`.  Issued even past the last tile
+  // (those read zeros), so every wave always has exactly 5 per tile in flight.
+  auto issue_tile = [&](int t, int sl) {
+    const uint32_t base = smem_lds + kRing + sl * KV_SLOT;
+    const uint32_t toff = (uint32_t)t * KV_TILE;
+#pragma unroll
+    for (int n = 0; n < KV_TLOADS; ++n) {
+      const int row0 = 16 * n + 4 * wave;
+      dma16(rq, base + row0 * kRowBytes, ld_voff[n] + toff);
+      dma16(rdo, base + KV_TILE + row0 * kRowBytes, ld_voff[n] + toff);
+    }
+    dma4(rLD, base + 2 * KV_TILE + 256 * wave, (uint32_t)(t * KV_BQ + lane) * 4);
+  };
+
+  // Per-lane LDS offsets, tile-relative:
+  //   row operands: row col, logical chunk 2 kc + h (V rows add 64 w + 32 g);
+  //   transpose reads: row 4 h + (lane % 16) / 4 (+ 8 e, + 16 u),
+  //   dims 32 mb + 16 ((lane / 16) % 2) + 4 (lane % 4).
+  int roff[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) roff[kc] = tile_off(col, 2 * kc + h);
+  int troff[4][2];
+  {
+    const int tr_s = lane & 15;
+    const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (tr_s & 3);
+    const int tr_row = 4 * h + (tr_s >> 2);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int dim = 32 * mb + tr_dim;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) troff[mb][e] = tile_off8(tr_row + 8 * e, dim >> 3, (dim >> 2) & 1);
+    }
+  }
+  const int vrow = 64 * wave * kRowBytes;  // this wave's rows of the V block
+
+  f32x16 dka[2][4], dva[2][4];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        dka[g][mb][i] = 0.f;
+        dva[g][mb][i] = 0.f;
+      }
 
   const int t0 = CAUSAL ? (k0 / KV_BQ) : 0;
   const int ntiles = (N + KV_BQ - 1) / KV_BQ;
 
-  auto issue_tile = [&](int t, int buf) {
-    char* base = stage0 + buf * KV_STAGE;
+  // P and dS of the previous tile, packed for the dV / dK products.  They
+  // start at zero: the first step multiplies them into a slot that holds
+  // zeros (cleared below) or an earlier tile, which adds nothing.
+  bf16x8 pb[2][2], sb[2][2];
 #pragma unroll
-    for (int n = 0; n < KV_BQ / 32; ++n) {
-      const int row0 = 32 * n + 4 * wave;
-      const int row = row0 + ld_sub;
-      const uint32_t voff = (uint32_t)(t * KV_BQ + row) * kRowBytes + ((ld_pc ^ swz(row)) << 4);
-      buf_load16_lds(rq, base + row0 * kRowBytes, voff);
-      buf_load16_lds(rdo, base + KV_TILE + row0 * kRowBytes, voff);
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      pb[g][u] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      sb[g][u] = pb[g][u];
     }
-    if (wave == 0) buf_load4_lds(rL, base + 2 * KV_TILE, (uint32_t)(t * KV_BQ + lane) * 4);
-    if (wave == 1) buf_load4_lds(rD, base + 2 * KV_TILE + KV_BQ * 4, (uint32_t)(t * KV_BQ + lane) * 4);
+
+  // dV^T += dO^T P and dK^T += Q^T dS for the tile in ring slot `psl`
+  // (transposed operands from transpose reads, one (mb, u) step ahead).
+  // tro: transpose-read lane offsets (troff, passed through opaque() by the
+  // caller outside the region the products are scheduled in).
+  auto dvdk = [&](int psl, const int (&tro)[4][2]) {
+    const int qsl = kRing + psl * KV_SLOT, osl = qsl + KV_TILE;
+    bf16x8 a_do[2], a_q[2];
+    auto rdt = [&](int n, int b) {
+      const int mb = n >> 1, ro2 = 16 * (n & 1) * kRowBytes;
+      a_do[b] = join(lds_read_tr(smem + osl + ro2 + tro[mb][0]), lds_read_tr(smem + osl + ro2 + tro[mb][1]));
+      a_q[b] = join(lds_read_tr(smem + qsl + ro2 + tro[mb][0]), lds_read_tr(smem + qsl + ro2 + tro[mb][1]));
+    };
+    rdt(0, 0);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int b = n & 1, mb = n >> 1, u = n & 1;
+      if (n < 7) rdt(n + 1, b ^ 1);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        dva[g][mb] = mfma32(a_do[b], pb[g][u], dva[g][mb]);
+        dka[g][mb] = mfma32(a_q[b], sb[g][u], dka[g][mb]);
+      }
+    }
   };
 
-  f32x16 dka[4], dva[4];
+  auto step = [&](int t, auto bc) {
+    constexpr int sl = decltype(bc)::value;
+    constexpr int psl = (sl + KV_NSLOT - 1) % KV_NSLOT;  // slot of tile t - 1
+    constexpr int qsl = kRing + sl * KV_SLOT;            // smem offsets of this slot's parts
+    constexpr int osl = qsl + KV_TILE;
+    constexpr int lsl = qsl + 2 * KV_TILE;
+    constexpr int dsl = lsl + 256;
+    // Tile t has landed once only tile t + 1's loads may be in flight; the
+    // barrier then publishes every wave's part of it and frees the slot that
+    // tile t - 2 used, which tile t + 2 takes (tile t - 1 is still read here).
+    ring_wait_barrier<KV_LOADS_PER_TILE>();
+    issue_tile(t + 2, (sl + 2) % KV_NSLOT);
+    const int qs = t * KV_BQ;
+    if (CAUSAL && qs < kw) return;  // every query of the tile precedes every key of the wave
+
+    // Lane offsets from three base registers: logical chunk bits only flip
+    // physical chunk bits under the XOR swizzle, so a row operand's chunk
+    // 2 kc + h sits at roff[0] ^ (32 kc) and a transpose read's dims 32 mb +
+    // ... at troff[0][e] ^ (64 mb).
+    const int ro0 = opaque(roff[0]);
+    const int rv0 = opaque(roff[0] + vrow);
+    const int tr0 = opaque(troff[0][0]), tr1 = opaque(troff[0][1]);
+    int ro[8];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+    for (int kc = 0; kc < 8; ++kc) ro[kc] = ro0 ^ (32 * kc);
+    int tro[4][2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dka[mb][i] = 0.f;
-      dva[mb][i] = 0.f;
+    for (int mb = 0; mb < 4; ++mb) {
+      tro[mb][0] = tr0 ^ (64 * mb);
+      tro[mb][1] = tr1 ^ (64 * mb);
     }
 
-  const int tr_s = lane & 15;
-  const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (tr_s & 3);
-  const int tr_row = 4 * h + (tr_s >> 2);
+    // S = Q K^T and dP = dO V^T, operands one k-step ahead.
+    f32x16 s[2], dp[2];
+    bf16x8 qa[2], da[2], va[2][2];
+    auto rd = [&](int kc, int b) {
+      qa[b] = __builtin_bit_cast(bf16x8, lds_read16(smem + qsl, ro[kc]));
+      da[b] = __builtin_bit_cast(bf16x8, lds_read16(smem + osl, ro[kc]));
+      // V rows: the chunk swizzle depends on the row only through col.
+      const int vo = rv0 ^ (32 * kc);
+      va[b][0] = __builtin_bit_cast(bf16x8, lds_read16(smem, vo));
+      va[b][1] = __builtin_bit_cast(bf16x8, lds_read16(smem + 32 * kRowBytes, vo));
+    };
+    rd(0, 0);
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const int b = kc & 1;
+      if (kc < 7) rd(kc + 1, b ^ 1);
+      if (kc == 0) {
+        mfma_v_init(s[0], qa[b], kf[0][kc]);
+        mfma_v_init(dp[0], da[b], va[b][0]);
+        mfma_v_init(s[1], qa[b], kf[1][kc]);
+        mfma_v_init(dp[1], da[b], va[b][1]);
+      } else {
+        mfma_v(s[0], qa[b], kf[0][kc]);
+        mfma_v(dp[0], da[b], va[b][0]);
+        mfma_v(s[1], qa[b], kf[1][kc]);
+        mfma_v(dp[1], da[b], va[b][1]);
+      }
+    }
+    mfma_v_fence(s[0], s[1], dp[0], dp[1]);
 
-  if (t0 < ntiles) issue_tile(t0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+    // Causal mask, only on the (at most two) tiles that cross the diagonal:
+    // S = -inf where the key follows the query, so P and dS come out zero.
+    // Element i of a lane is query qs + 8 (i / 4) + 4 h + i % 4 against key
+    // kw + 32 g + col.
+    if (CAUSAL && qs < kw + 64) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int key = kw + 32 * g + col;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (key > qs + 8 * (i >> 2) + 4 * h + (i & 3)) s[g][i] = -INFINITY;
+      }
+    }
 
-  for (int t = t0; t < ntiles; ++t) {
-    const int buf = (t - t0) & 1;
-    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
-    const char* qb = stage0 + buf * KV_STAGE;
-    const char* dob = qb + KV_TILE;
-    const float* lsb = reinterpret_cast<const float*>(qb + 2 * KV_TILE);
-    const float* dsb = lsb + KV_BQ;
-    const int qs = t * KV_BQ + 32 * qh;
-    const bool active = !CAUSAL || (qs + 31 >= kw);
-    if (active) {
-      f32x16 s, dp;
+    // P = exp2(S scale log2(e) - L log2(e)), dS = P (dP - D), interleaved
+    // by hand with the dV / dK products of the previous tile: product step
+    // n (4 MFMAs) carries the softmax of row group n / 2, key group n % 2,
+    // one element per MFMA; sched_barrier keeps the compiler to that order.
+    const float* lb = reinterpret_cast<const float*>(smem + lsl);
+    const float* db = reinterpret_cast<const float*>(smem + dsl);
+    const int pq = kRing + psl * KV_SLOT, po = pq + KV_TILE;
+    bf16x8 npb[2][2], nsb[2][2];
+    bf16x8 a_do[2], a_q[2];
+    f32x4 l4[2], d4[2];
+    auto rdt = [&](int n, int b) {
+      const int mb = n >> 1, ro2 = 16 * (n & 1) * kRowBytes;
+      a_do[b] = join(lds_read_tr(smem + po + ro2 + tro[mb][0]), lds_read_tr(smem + po + ro2 + tro[mb][1]));
+      a_q[b] = join(lds_read_tr(smem + pq + ro2 + tro[mb][0]), lds_read_tr(smem + pq + ro2 + tro[mb][1]));
+    };
+    auto rdl = [&](int gg) {
+      const int r = 8 * gg + 4 * h;
+      l4[gg & 1] = *reinterpret_cast<const f32x4*>(lb + r);
+      d4[gg & 1] = *reinterpret_cast<const f32x4*>(db + r);
+    };
+    rdt(0, 0);
+    rdl(0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[i] = 0.f;
-        dp[i] = 0.f;
+    for (int n = 0; n < 8; ++n) {
+      const int b = n & 1, mb = n >> 1, u = n & 1;
+      const int gg = n >> 1, g = n & 1;
+      if (n < 7) rdt(n + 1, b ^ 1);
+      if (g == 1 && gg < 3) rdl(gg + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int gk = k >> 1;
+        if ((k & 1) == 0)
+          dva[gk][mb] = mfma32(a_do[b], pb[gk][u], dva[gk][mb]);
+        else
+          dka[gk][mb] = mfma32(a_q[b], sb[gk][u], dka[gk][mb]);
+        const int i = 4 * gg + k;
+        const float p = fast_exp2(__builtin_fmaf(s[g][i], sl2, -l4[gg & 1][k]));
+        s[g][i] = p;
+        dp[g][i] = p * (dp[g][i] - d4[gg & 1][k]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        const int qoff = tile_off(32 * qh + col, 2 * kc + h);
-        const int koff = tile_off(32 * kg + col, 2 * kc + h);
-        s = mfma32(__builtin_bit_cast(bf16x8, lds_read16(qb, qoff)),
-                   __builtin_bit_cast(bf16x8, lds_read16(kblk, koff)), s);
-        dp = mfma32(__builtin_bit_cast(bf16x8, lds_read16(dob, qoff)),
-                    __builtin_bit_cast(bf16x8, lds_read16(vblk, koff)), dp);
+      // Rows 8 v .. 8 v + 7 of key group g are done after row group 2 v + 1.
+      if (gg & 1) {
+        const int v = gg >> 1, e = 8 * v;
+        npb[g][v] = pack8(s[g][e], s[g][e + 1], s[g][e + 2], s[g][e + 3], s[g][e + 4], s[g][e + 5],
+                          s[g][e + 6], s[g][e + 7]);
+        nsb[g][v] = pack8(dp[g][e], dp[g][e + 1], dp[g][e + 2], dp[g][e + 3], dp[g][e + 4],
+                          dp[g][e + 5], dp[g][e + 6], dp[g][e + 7]);
       }
-      const bool need_mask = CAUSAL && (qs < kw + 31);
+    }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r = 32 * qh + 8 * g + 4 * h;  // tile-local query row of element 4g
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lsb + r);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsb + r);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 4 * g + j;
-          float p = fast_exp2(__builtin_fmaf(s[i], sl2, -l4[j]));
-          if (need_mask && krow > t * KV_BQ + r + j) p = 0.f;
-          s[i] = p;
-          dp[i] = p * (dp[i] - d4[j]);
-        }
-      }
-      bf16x8 pb[2], sb[2];
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int b = 8 * u;
-        pb[u] = pack8(s[b], s[b + 1], s[b + 2], s[b + 3], s[b + 4], s[b + 5], s[b + 6], s[b + 7]);
-        sb[u] = pack8(dp[b], dp[b + 1], dp[b + 2], dp[b + 3], dp[b + 4], dp[b + 5], dp[b + 6],
-                      dp[b + 7]);
+        pb[g][u] = npb[g][u];
+        sb[g][u] = nsb[g][u];
       }
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int dim = 32 * mb + tr_dim;
-        const int chunk = dim >> 3;
-        const int half = (dim >> 2) & 1;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = 32 * qh + 16 * u + tr_row;
-          const bf16x8 a_do = join(lds_read_tr(dob + tile_off8(r, chunk, half)),
-                                   lds_read_tr(dob + tile_off8(r + 8, chunk, half)));
-          dva[mb] = mfma32(a_do, pb[u], dva[mb]);
-          const bf16x8 a_q = join(lds_read_tr(qb + tile_off8(r, chunk, half)),
-                                  lds_read_tr(qb + tile_off8(r + 8, chunk, half)));
-          dka[mb] = mfma32(a_q, sb[u], dka[mb]);
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
+  };
 
-  // Sum the two query halves: waves 4..7 park their partials in LDS (the loop
-  // is over, every buffer is free), waves 0..3 add them and store.
-  float* red = reinterpret_cast<float*>(smem) + kg * 2 * 64 * 64;  // 32 KiB per key group
-  if (qh == 1) {
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        red[(mb * 16 + i) * 64 + lane] = dka[mb][i];
-        red[64 * 64 + (mb * 16 + i) * 64 + lane] = dva[mb][i];
-      }
+  // Slot 3 feeds the first step's dV / dK products: clear it.
+  {
+    char* z = smem + kRing + 3 * KV_SLOT;
+    for (int o = tid * 16; o < 2 * KV_TILE; o += KV_THREADS * 16) lds_write16(z, o, u32x4{0u, 0u, 0u, 0u});
   }
-  __syncthreads();
-  if (qh == 0) {
+  issue_tile(t0, 0);
+  issue_tile(t0 + 1, 1);
+  for (int t = t0; t < ntiles; t += 4) {
+    step(t, kv_ic<0>{});
+    if (t + 1 < ntiles) step(t + 1, kv_ic<1>{});
+    if (t + 2 < ntiles) step(t + 2, kv_ic<2>{});
+    if (t + 3 < ntiles) step(t + 3, kv_ic<3>{});
+  }
+  // The last tile's dV / dK products.
+  if (ntiles > t0) {
+    const int lsl_ = (ntiles - 1 - t0) & 3;
+    __syncthreads();
+    dvdk(lsl_, troff);
+  }
+  dma_drain();  // no LDS-direct load may outlive the workgroup
+
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        dka[mb][i] += red[(mb * 16 + i) * 64 + lane];
-        dva[mb][i] += red[64 * 64 + (mb * 16 + i) * 64 + lane];
-      }
+  for (int g = 0; g < 2; ++g) {
+    const int krow = kw + 32 * g + col;
     if (krow < N) {
       char* dkrow = reinterpret_cast<char*>(dk + head) + (size_t)krow * kRowBytes;
       char* dvrow = reinterpret_cast<char*>(dv + head) + (size_t)krow * kRowBytes;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int i = 4 * g;
-          const int off = (32 * mb + 8 * g + 4 * h) * 2;
-          u32x2 wk = {pack_bf16(dka[mb][i] * scale, dka[mb][i + 1] * scale),
-                      pack_bf16(dka[mb][i + 2] * scale, dka[mb][i + 3] * scale)};
-          u32x2 wv = {pack_bf16(dva[mb][i], dva[mb][i + 1]), pack_bf16(dva[mb][i + 2], dva[mb][i + 3])};
+        for (int gg = 0; gg < 4; ++gg) {
+          const int i = 4 * gg;
+          const int off = (32 * mb + 8 * gg + 4 * h) * 2;
+          u32x2 wk = {pack_bf16(dka[g][mb][i] * scale, dka[g][mb][i + 1] * scale),
+                      pack_bf16(dka[g][mb][i + 2] * scale, dka[g][mb][i + 3] * scale)};
+          u32x2 wv = {pack_bf16(dva[g][mb][i], dva[g][mb][i + 1]),
+                      pack_bf16(dva[g][mb][i + 2], dva[g][mb][i + 3])};
           *reinterpret_cast<u32x2*>(dkrow + off) = wk;
           *reinterpret_cast<u32x2*>(dvrow + off) = wv;
         }
@@ -444,14 +650,7 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
   const int nkb = (N + KV_BK - 1) / KV_BK;
   dim3 grid((unsigned)(nkb * BH)), block(KV_THREADS);
   auto kern = causal ? bwd_dkdv_kernel<true> : bwd_dkdv_kernel<false>;
-  static bool attr_set[2] = {false, false};
-  if (!attr_set[causal]) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, KV_SMEM);
-    if (e != hipSuccess) return e;
-    attr_set[causal] = true;
-  }
-  hipLaunchKernelGGL(kern, grid, block, KV_SMEM, stream, static_cast<const uint16_t*>(q),
+  hipLaunchKernelGGL(kern, grid, block, 0, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                      static_cast<const uint16_t*>(dO), ws, static_cast<uint16_t*>(dk),
                      static_cast<uint16_t*>(dv), BH, N, sl2, scale);

@@ -1,0 +1,31 @@
+"""The build-time check of inline-assembly MFMAs (exact_io_aware_10_amd/asm_check.py)
+flags a result read inside the MFMA's write window and accepts fenced code."""
+from exact_io_aware_10_amd import asm_check
+
+MFMA = """;;#ASMSTART
+\tv_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]
+;;#ASMEND
+"""
+
+
+def test_early_valu_read_is_flagged():
+    assert len(asm_check.check(MFMA + "\tv_add_f32_e32 v30, v1, v2\n")) == 1
+
+
+def test_early_copy_of_agpr_result_is_flagged():
+    text = MFMA.replace("v[0:15]", "a[0:15]") + "\tv_accvgpr_mov_b32 a200, a15\n"
+    assert len(asm_check.check(text)) == 1
+
+
+def test_fenced_read_is_accepted():
+    assert asm_check.check(MFMA + "\ts_nop 15\n\tv_add_f32_e32 v30, v1, v2\n") == []
+
+
+def test_unrelated_registers_and_chains_are_accepted():
+    text = MFMA + MFMA + "\tv_add_f32_e32 v30, v40, v41\n"
+    assert asm_check.check(text) == []
+
+
+def test_compiler_mfma_is_not_checked():
+    text = "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]\n\tv_add_f32_e32 v30, v1, v2\n"
+    assert asm_check.check(text) == []
