@@ -481,33 +481,72 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
 // ---------------------------------------------------------------------------
 // dQ
+//
+// One wave per SIMD, four waves per workgroup: wave w owns queries
+// q0 + 64 w .. + 63 as two groups of 32, with their Q and dO fragments (the B
+// operands of S^T = K Q^T and dP^T = V dO^T) loaded once, Q into AGPRs, and
+// the dQ^T accumulators (128 registers) in AGPRs as well.  32-key tiles of K and V
+// stream through a four-slot LDS ring.  Owning 64 queries lets every K or V
+// fragment read from LDS feed two MFMAs.  Per tile t and wave:
+//   A  S^T  = K_t Q^T      16 MFMAs (VGPR accumulators, inline assembly)
+//   B  dP^T = V_t dO^T     16 MFMAs, interleaved with P = exp2(S scale log2 e
+//                          - L log2 e) of tile t
+//   C  dQ^T += K_{t-1}^T dS_{t-1}^T   16 MFMAs, interleaved with
+//                          dS = P (dP - D) of tile t, packed to bf16
 // ---------------------------------------------------------------------------
-constexpr int DQ_BQ = 128;   // queries per workgroup
-constexpr int DQ_WAVES = 4;  // 32 queries per wave
-constexpr int DQ_BC = 64;    // keys per streamed tile (two 32-key halves)
-constexpr int DQ_TILE = DQ_BC * kRowBytes;
+constexpr int DQ_QW = 64;                    // queries per wave
+constexpr int DQ_WAVES = 4;
+constexpr int DQ_BQ = DQ_QW * DQ_WAVES;      // queries per workgroup
+constexpr int DQ_BK = 32;                    // keys per streamed tile
+constexpr int DQ_TILE = DQ_BK * kRowBytes;   // 8 KiB (K or V)
 constexpr int DQ_THREADS = DQ_WAVES * 64;
-constexpr int DQ_LOADS = DQ_TILE / 1024 / DQ_WAVES;
+constexpr int DQ_TLOADS = DQ_TILE / 1024 / DQ_WAVES;  // LDS-direct loads per wave per tensor
+constexpr int DQ_SLOT = 2 * DQ_TILE;                  // K tile, then V tile
+constexpr int DQ_NSLOT = 4;
+constexpr int DQ_SMEM = DQ_NSLOT * DQ_SLOT;           // 64 KiB
+constexpr int DQ_LOADS_PER_TILE = 2 * DQ_TLOADS;
+
+// S^T / dP^T MFMA with the B operand (Q^T or dO^T) in AGPRs and the result in
+// VGPRs; hazards as for mfma_v (s_fence2 after the last one).
+__device__ __forceinline__ void mfma_va0(f32x16& c, bf16x8 a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b) : "memory");
+}
+__device__ __forceinline__ void mfma_va(f32x16& c, bf16x8 a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b) : "memory");
+}
+// dQ^T += A B with the accumulator in AGPRs (fenced by acc_fence8).
+__device__ __forceinline__ void mfma_aa(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void acc_fence8(f32x16 (&c)[2][4]) {
+  asm volatile("s_nop 15"
+               : "+a"(c[0][0]), "+a"(c[0][1]), "+a"(c[0][2]), "+a"(c[0][3]), "+a"(c[1][0]),
+                 "+a"(c[1][1]), "+a"(c[1][2]), "+a"(c[1][3]));
+}
+__device__ __forceinline__ void s_fence2(f32x16& c0, f32x16& c1) {
+  asm volatile("s_nop 15" : "+v"(c0), "+v"(c1));
+}
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(DQ_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(DQ_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
                    const float* __restrict__ ws, uint16_t* __restrict__ dq, int BH, int N, int nqb,
                    float sl2, float scale) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * DQ_TILE];
+  __shared__ __attribute__((aligned(16))) char smem[DQ_SMEM];
+  const uint32_t smem_lds = lds_addr(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
   const int col = lane & 31;
 
+  // Causal: issue the longest query blocks first.
   int qblk, bh;
   block_head(blockIdx.x, nqb, BH, CAUSAL, &qblk, &bh);
   const int q0 = qblk * DQ_BQ;
-  const int q0w = q0 + wave * 32;
-  const int qrow = q0w + col;
+  const int q0w = q0 + DQ_QW * wave;
 
   const size_t head = (size_t)bh * (size_t)N * kD;
   const uint32_t head_bytes = (uint32_t)N * kRowBytes;
@@ -519,117 +558,241 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const rsrc_t rD = make_rsrc(ws + (size_t)bh * N, (uint32_t)N * 4);
   const rsrc_t rL = make_rsrc(ws + rows + (size_t)bh * N, (uint32_t)N * 4);
 
-  bf16x8 qf[8], df[8];
+  // Q^T and dO^T as B operands (zero past N), Q straight into AGPRs: lane
+  // holds Q[q0w + 32 g + col][16 kc + 8 h .. + 7].  Waited for below.
+  bf16x8 qf[2][8], df[2][8];
 #pragma unroll
-  for (int kc = 0; kc < 8; ++kc) {
-    const uint32_t off = (uint32_t)qrow * kRowBytes + (2 * kc + h) * 16;
-    qf[kc] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
-    df[kc] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const uint32_t off = (uint32_t)(q0w + 32 * g + col) * kRowBytes + (2 * kc + h) * 16;
+      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=a"(qf[g][kc]) : "v"(off), "s"(rq) : "memory");
+      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(df[g][kc]) : "v"(off), "s"(rdo) : "memory");
+    }
+  float l2[2], dd[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    l2[g] = buf_load_f32(rL, (uint32_t)(q0w + 32 * g + col) * 4);
+    dd[g] = buf_load_f32(rD, (uint32_t)(q0w + 32 * g + col) * 4);
   }
-  const float l2 = buf_load_f32(rL, (uint32_t)qrow * 4);
-  const float Dq = buf_load_f32(rD, (uint32_t)qrow * 4);
+  // Wait for L and D here, in the compiler's view as well, before any
+  // LDS-direct load (invisible to it) is in flight.
+  asm volatile("" : : "v"(l2[0]), "v"(l2[1]), "v"(dd[0]), "v"(dd[1]));
 
+  // Tiles the workgroup streams, and tiles this wave computes on.
   const int kend = CAUSAL ? min(N, q0 + DQ_BQ) : N;
-  const int ntiles = (kend + DQ_BC - 1) / DQ_BC;
+  const int nt = (kend + DQ_BK - 1) / DQ_BK;
+  const int wend = CAUSAL ? min(N, q0w + DQ_QW) : N;
+  const int tw = (q0w < N) ? (wend + DQ_BK - 1) / DQ_BK : 0;
+  // First tile that needs an element-wise mask (causal diagonal or keys >= N).
+  const int tmask = CAUSAL ? min(q0w / DQ_BK, N / DQ_BK) : N / DQ_BK;
 
+  // Tile loader: instruction n of wave w fills rows 16 n + 4 w .. + 3 of the
+  // K and V tiles of a slot (rows past N read as zero).
   const int ld_sub = lane >> 4;
   const int ld_pc = lane & 15;
-  auto issue_tile = [&](int t, int buf) {
-    char* kb = smem + buf * 2 * DQ_TILE;
-    char* vb = kb + DQ_TILE;
+  uint32_t ld_voff[DQ_TLOADS];
 #pragma unroll
-    for (int n = 0; n < DQ_LOADS; ++n) {
+  for (int n = 0; n < DQ_TLOADS; ++n) {
+    const int row = 16 * n + 4 * wave + ld_sub;
+    ld_voff[n] = (uint32_t)row * kRowBytes + ((ld_pc ^ swz(row)) << 4);
+  }
+  auto issue_tile = [&](int t, int sl) {
+    const uint32_t base = smem_lds + sl * DQ_SLOT;
+    const uint32_t toff = (uint32_t)t * DQ_TILE;
+#pragma unroll
+    for (int n = 0; n < DQ_TLOADS; ++n) {
       const int row0 = 16 * n + 4 * wave;
-      const int row = row0 + ld_sub;
-      const uint32_t voff = (uint32_t)(t * DQ_BC + row) * kRowBytes + ((ld_pc ^ swz(row)) << 4);
-      buf_load16_lds(rk, kb + row0 * kRowBytes, voff);
-      buf_load16_lds(rv, vb + row0 * kRowBytes, voff);
+      dma16(rk, base + row0 * kRowBytes, ld_voff[n] + toff);
+      dma16(rv, base + DQ_TILE + row0 * kRowBytes, ld_voff[n] + toff);
     }
   };
 
-  f32x16 acc[4];
+  // Per-lane LDS offsets, tile-relative:
+  //   row operands (K, V): row col, logical chunk 2 kc + h;
+  //   K^T transpose reads: row 4 h + (lane % 16) / 4 (+ 8 e, + 16 u),
+  //   dims 32 mb + 16 ((lane / 16) % 2) + 4 (lane % 4).
+  int roff[8];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int kc = 0; kc < 8; ++kc) roff[kc] = tile_off(col, 2 * kc + h);
+  int troff[4][2];
+  {
+    const int tr_s = lane & 15;
+    const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (tr_s & 3);
+    const int tr_row = 4 * h + (tr_s >> 2);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
-
-  const int tr_s = lane & 15;
-  const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (tr_s & 3);
-  const int tr_row = 4 * h + (tr_s >> 2);
-
-  issue_tile(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
-    const int k0 = t * DQ_BC;
-    const char* kb = smem + buf * 2 * DQ_TILE;
-    const char* vb = kb + DQ_TILE;
+    for (int mb = 0; mb < 4; ++mb) {
+      const int dim = 32 * mb + tr_dim;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int ks = k0 + 32 * st;
-      const bool active = !CAUSAL || (ks <= q0w + 31);
-      if (!active) continue;
-      f32x16 s, dp;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[i] = 0.f;
-        dp[i] = 0.f;
-      }
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc) {
-        const int off = tile_off(32 * st + col, 2 * kc + h);
-        s = mfma32(__builtin_bit_cast(bf16x8, lds_read16(kb, off)), qf[kc], s);
-        dp = mfma32(__builtin_bit_cast(bf16x8, lds_read16(vb, off)), df[kc], dp);
-      }
-      const bool need_mask = (CAUSAL && (ks + 31 > q0w)) || (ks + 32 > N);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(__builtin_fmaf(s[i], sl2, -l2));
-        if (need_mask) {
-          const int key = ks + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
-        }
-        dp[i] = p * (dp[i] - Dq);
-      }
-      bf16x8 sb[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int b = 8 * u;
-        sb[u] = pack8(dp[b], dp[b + 1], dp[b + 2], dp[b + 3], dp[b + 4], dp[b + 5], dp[b + 6],
-                      dp[b + 7]);
-      }
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int dim = 32 * mb + tr_dim;
-        const int chunk = dim >> 3;
-        const int half = (dim >> 2) & 1;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = 32 * st + 16 * u + tr_row;
-          const bf16x8 a = join(lds_read_tr(kb + tile_off8(r, chunk, half)),
-                                lds_read_tr(kb + tile_off8(r + 8, chunk, half)));
-          acc[mb] = mfma32(a, sb[u], acc[mb]);
-        }
-      }
+      for (int e = 0; e < 2; ++e) troff[mb][e] = tile_off8(tr_row + 8 * e, dim >> 3, (dim >> 2) & 1);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   }
 
-  if (qrow < N) {
-    char* row = reinterpret_cast<char*>(dq + head) + (size_t)qrow * kRowBytes;
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int i = 4 * g;
-        u32x2 w = {pack_bf16(acc[mb][i] * scale, acc[mb][i + 1] * scale),
-                   pack_bf16(acc[mb][i + 2] * scale, acc[mb][i + 3] * scale)};
-        *reinterpret_cast<u32x2*>(row + (32 * mb + 8 * g + 4 * h) * 2) = w;
+      for (int i = 0; i < 16; ++i) acc[g][mb][i] = 0.f;
+
+  // dS^T of the previous tile as B operands [group][key half]; zero before the
+  // first tile, whose products read the K part of slot 3, cleared below.
+  bf16x8 sb[2][2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) sb[g][u] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+
+  // Causal / tail mask of tile t on s: element i of a lane is key
+  // 32 t + 4 h + c_i, c_i = 8 (i / 4) + i % 4, masked when c_i >= lim.
+  auto mask_tile = [&](int t, f32x16 (&s)[2]) {
+    const int base = t * DQ_BK + 4 * h;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      int lim = N - base;
+      if (CAUSAL) lim = min(lim, q0w + 32 * g + col - base + 1);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + (i & 3) >= lim) s[g][i] = -INFINITY;
+    }
+  };
+
+  // dQ^T += K^T dS^T for the tile in slot psl (phase C), with sb.
+  auto dq_products = [&](int psl, auto&& between) {
+    const char* kt = smem + psl * DQ_SLOT;
+    bf16x8 a[2];
+    auto rdt = [&](int n, int b) {
+      const int mb = n & 3, u = n >> 2;
+      const char* rb = kt + 16 * u * kRowBytes;
+      a[b] = join(lds_read_tr(rb + troff[mb][0]), lds_read_tr(rb + troff[mb][1]));
+    };
+    rdt(0, 0);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int b = n & 1, mb = n & 3, u = n >> 2;
+      if (n < 7) rdt(n + 1, b ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        mfma_aa(acc[g][mb], a[b], sb[g][u]);
+        between(2 * n + g);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    // In the same basic block as the MFMAs: later accesses to the
+    // accumulators, the register allocator's copies included, come after it.
+    acc_fence8(acc);
+  };
+
+  // Step t (slot SL = t % 4): phases A, B, C as described above; the dQ
+  // products of phase C belong to tile t - 1 (zero dS before the first tile).
+  auto step = [&](int t) {
+    const int SL = t & (DQ_NSLOT - 1);
+    const int PSL = (t - 1) & (DQ_NSLOT - 1);
+    // Tile t has landed once only tile t + 1's loads may be in flight; the
+    // barrier publishes it and frees the slot of tile t - 2, which tile t + 2
+    // takes (tile t - 1 is still read here, in phase C).
+    ring_wait_barrier<DQ_LOADS_PER_TILE>();
+    issue_tile(t + 2, (SL + 2) % DQ_NSLOT);
+    const char* kb = smem + SL * DQ_SLOT;
+    const char* vb = kb + DQ_TILE;
+
+    // Phase A: S^T for both query groups, K fragments one step ahead.
+    f32x16 s[2], dp[2];
+    bf16x8 ka[2], va[2];
+    ka[0] = __builtin_bit_cast(bf16x8, lds_read16(kb, roff[0]));
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const int b = kc & 1;
+      if (kc < 7) ka[b ^ 1] = __builtin_bit_cast(bf16x8, lds_read16(kb, roff[kc + 1]));
+      if (kc == 6) va[0] = __builtin_bit_cast(bf16x8, lds_read16(vb, roff[0]));
+      if (kc == 0) {
+        mfma_va0(s[0], ka[b], qf[0][kc]);
+        mfma_va0(s[1], ka[b], qf[1][kc]);
+      } else {
+        mfma_va(s[0], ka[b], qf[0][kc]);
+        mfma_va(s[1], ka[b], qf[1][kc]);
+      }
+    }
+    s_fence2(s[0], s[1]);
+    if (t >= tmask) mask_tile(t, s);
+
+    // Phase B: dP^T, with P = exp2(S scale log2 e - L log2 e) in between
+    // (two scores per MFMA, written over S).
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const int b = kc & 1;
+      if (kc < 7) va[b ^ 1] = __builtin_bit_cast(bf16x8, lds_read16(vb, roff[kc + 1]));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        if (kc == 0)
+          mfma_v_init(dp[g], va[b], df[g][kc]);
+        else
+          mfma_v(dp[g], va[b], df[g][kc]);
+        const int idx = 2 * (2 * kc + g);  // scores idx, idx + 1 of the 32
+        const int sg = idx >> 4, si = idx & 15;
+        s[sg][si] = fast_exp2(__builtin_fmaf(s[sg][si], sl2, -l2[sg]));
+        s[sg][si + 1] = fast_exp2(__builtin_fmaf(s[sg][si + 1], sl2, -l2[sg]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    s_fence2(dp[0], dp[1]);
+
+    // Phase C: dQ products of tile t - 1, with dS = P (dP - D) of tile t in
+    // between, packed into the next step's B operands.
+    uint32_t w[2][8];
+    dq_products(PSL, [&](int m) {
+      const int idx = 2 * m;
+      const int sg = idx >> 4, si = idx & 15;
+      const float d0 = s[sg][si] * (dp[sg][si] - dd[sg]);
+      const float d1 = s[sg][si + 1] * (dp[sg][si + 1] - dd[sg]);
+      w[sg][si >> 1] = pack_bf16(d0, d1);
+      asm volatile("" : "+v"(w[sg][si >> 1]));  // convert here, not after the loop
+    });
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        sb[g][u] = __builtin_bit_cast(bf16x8, u32x4{w[g][4 * u], w[g][4 * u + 1], w[g][4 * u + 2], w[g][4 * u + 3]});
+  };
+
+  // Slot 3 feeds the first step's dQ products: clear its K tile.
+  {
+    char* z = smem + 3 * DQ_SLOT;
+    for (int o = tid * 16; o < DQ_TILE; o += DQ_THREADS * 16) lds_write16(z, o, u32x4{0u, 0u, 0u, 0u});
+  }
+  issue_tile(0, 0);
+  issue_tile(1, 1);
+  for (int t = 0; t < tw; ++t) step(t);
+  // Step tw: the last tile's dQ products; then the wave only keeps the ring
+  // going up to the workgroup's step nt.
+  for (int tt = tw; tt <= nt; ++tt) {
+    ring_wait_barrier<DQ_LOADS_PER_TILE>();
+    issue_tile(tt + 2, (tt + 2) % DQ_NSLOT);
+    if (tt == tw && tw > 0) dq_products((tw - 1) % DQ_NSLOT, [](int) {});
+  }
+  dma_drain();  // no LDS-direct load may outlive the workgroup
+
+  if (tw > 0) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int qrow = q0w + 32 * g + col;
+      if (qrow < N) {
+        char* row = reinterpret_cast<char*>(dq + head) + (size_t)qrow * kRowBytes;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            const int i = 4 * gg;
+            u32x2 wv = {pack_bf16(acc[g][mb][i] * scale, acc[g][mb][i + 1] * scale),
+                        pack_bf16(acc[g][mb][i + 2] * scale, acc[g][mb][i + 3] * scale)};
+            *reinterpret_cast<u32x2*>(row + (32 * mb + 8 * gg + 4 * h) * 2) = wv;
+          }
+      }
+    }
   }
 }
 
