@@ -97,7 +97,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=40,
+                    help="untimed steps first; about 0.2 s lets the clocks settle")
     ap.add_argument("--workload", default="causal_b1_h64_n8192", choices=sorted(fa_inputs.WORKLOADS))
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle timing sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")

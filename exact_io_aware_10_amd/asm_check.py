@@ -4,10 +4,13 @@ Some MFMAs in the kernels are written as inline assembly (accumulators kept
 in VGPRs or AGPRs against the compiler's own choice).  The compiler's hazard
 recognizer does not look inside inline assembly, so nothing stops the
 register allocator from placing a copy of such an MFMA's result right after
-it, before the matrix core has written the result.  The kernels bracket those
+it, before the matrix core has written the result; nor does anything stop it
+from overwriting the registers such an MFMA reads as its accumulator input
+(srcC) while the matrix core is still reading them.  The kernels bracket those
 MFMAs with fences; this check verifies the generated code: no instruction may
-read or overwrite the destination registers of an inline-assembly MFMA within
-MIN_WAIT wait states of it (an 8-pass 32x32 MFMA needs about 11).
+read or overwrite the destination registers of an inline-assembly MFMA, nor
+write its srcC registers, within MIN_WAIT wait states of it (an 8-pass 32x32
+MFMA needs about 11 for the first and fewer for the second).
 
 Usage: python -m exact_io_aware_10_amd.asm_check FILE.s ...
 """
@@ -47,14 +50,28 @@ def _parse(text: str):
     return insts
 
 
+def _written(op: str, ops: list) -> set:
+    """VGPRs / AGPRs an instruction writes (its first operand, where that is a
+    destination: VALU and MFMA results, LDS and buffer loads into registers)."""
+    if not ops:
+        return set()
+    if op.startswith("v_") or op.startswith(("ds_read", "ds_load")) or (
+            op.startswith(("buffer_load", "global_load", "flat_load", "scratch_load"))
+            and "lds" not in ops):
+        return _regs(ops[0])
+    return set()
+
+
 def check(text: str, min_wait: int = MIN_WAIT) -> list[str]:
-    """Return one message per early access to an inline-asm MFMA result."""
+    """Return one message per early access to an inline-asm MFMA's result, or
+    early overwrite of its srcC registers."""
     insts = _parse(text)
     problems = []
     for idx, (ln, op, ops, in_asm) in enumerate(insts):
         if not (in_asm and op.startswith("v_mfma")):
             continue
         dst = _regs(ops[0])
+        srcc = _regs(ops[3]) - dst if len(ops) > 3 else set()
         waited = 0
         for ln2, op2, ops2, _ in insts[idx + 1:]:
             waited += int(ops2[0], 0) + 1 if op2 == "s_nop" else 1
@@ -63,6 +80,10 @@ def check(text: str, min_wait: int = MIN_WAIT) -> list[str]:
             touched = set()
             for tok in ops2:
                 touched |= _regs(tok)
+            if srcc & _written(op2, ops2):
+                problems.append(f"line {ln}: {op} srcC {ops[3]} is overwritten {waited} wait states "
+                                f"later at line {ln2}: {op2} {' '.join(ops2)}")
+                break
             if op2.startswith("v_mfma") and _regs(ops2[0]) == dst and ops2[3:4] == [ops[0]]:
                 continue  # accumulation chain into the same registers: forwarded
             if dst & touched:

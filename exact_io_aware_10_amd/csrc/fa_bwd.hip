@@ -128,14 +128,23 @@ constexpr int KV_VBLK = KV_BK * kRowBytes;   // 64 KiB
 constexpr int KV_THREADS = KV_WAVES * 64;
 constexpr int KV_TLOADS = KV_TILE / 1024 / KV_WAVES;  // LDS-direct loads per wave per tensor
 constexpr int KV_VLOADS = KV_VBLK / 1024 / KV_WAVES;
-// Ring slot: Q tile, dO tile, then four 64-entry float arrays (L log2(e), D,
-// and two sinks): the 4-byte LDS-direct load writes one entry per lane, and
-// every wave issues one so that all waves issue the same number of loads.
-constexpr int KV_SLOT = 2 * KV_TILE + 4 * 256;
+// LDS layout: the ring's Q / dO tiles first, so that every constant offset
+// into them fits the 16-bit offset field of LDS instructions (no address
+// adds); then per slot four 64-entry float arrays (L log2(e), D, and two
+// sinks: the 4-byte LDS-direct load writes one entry per lane, and every wave
+// issues one so that all waves issue the same number of loads); then the V
+// block, addressed from a base register.
 constexpr int KV_NSLOT = 4;
+constexpr int KV_SLOT = 2 * KV_TILE;                       // Q tile, dO tile
+constexpr int KV_LD_OFF = KV_NSLOT * KV_SLOT;              // 64 KiB
+constexpr int KV_LD_SLOT = 4 * 256;
+constexpr int KV_V_OFF = KV_LD_OFF + KV_NSLOT * KV_LD_SLOT;
 constexpr int KV_LOADS_PER_TILE = 2 * KV_TLOADS + 1;
 static_assert(KV_LOADS_PER_TILE == 5, "the ring wait below counts 5 loads per tile");
-constexpr int KV_SMEM = KV_VBLK + KV_NSLOT * KV_SLOT;
+static_assert((KV_NSLOT - 1) * KV_SLOT + KV_TILE + KV_TILE / 2 < 65536,
+              "ring offsets must fit the LDS offset field");
+static_assert(KV_V_OFF % 256 == 0, "the V base must leave the chunk-swizzle bits free");
+constexpr int KV_SMEM = KV_V_OFF + KV_VBLK;
 
 template <int V>
 struct kv_ic {
@@ -157,7 +166,6 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                      uint16_t* __restrict__ dv, int BH, int N, float sl2, float scale) {
   __shared__ __attribute__((aligned(16))) char smem[KV_SMEM];
   const uint32_t smem_lds = lds_addr(smem);  // LDS byte address of smem (wave-uniform)
-  constexpr int kRing = KV_VBLK;              // byte offset of the ring in smem
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -189,7 +197,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   for (int n = 0; n < KV_VLOADS; ++n) {
     const int row0 = 16 * n + 4 * wave;
     const int row = row0 + ld_sub;
-    dma16(rv, smem_lds + row0 * kRowBytes, (uint32_t)(k0 + row) * kRowBytes + ((ld_pc ^ swz(row)) << 4));
+    dma16(rv, smem_lds + KV_V_OFF + row0 * kRowBytes,
+          (uint32_t)(k0 + row) * kRowBytes + ((ld_pc ^ swz(row)) << 4));
   }
   // K as the B operand of S = Q K^T: lane holds K[kw + 32 g + col][16 kc + 8 h .. + 7].
   bf16x8 kf[2][8];
@@ -215,7 +224,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // Loads of tile t into ring slot `sl`.  Issued even past the last tile
   // (those read zeros), so every wave always has exactly 5 per tile in flight.
   auto issue_tile = [&](int t, int sl) {
-    const uint32_t base = smem_lds + kRing + sl * KV_SLOT;
+    const uint32_t base = smem_lds + sl * KV_SLOT;
     const uint32_t toff = (uint32_t)t * KV_TILE;
 #pragma unroll
     for (int n = 0; n < KV_TLOADS; ++n) {
@@ -223,7 +232,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       dma16(rq, base + row0 * kRowBytes, ld_voff[n] + toff);
       dma16(rdo, base + KV_TILE + row0 * kRowBytes, ld_voff[n] + toff);
     }
-    dma4(rLD, base + 2 * KV_TILE + 256 * wave, (uint32_t)(t * KV_BQ + lane) * 4);
+    dma4(rLD, smem_lds + KV_LD_OFF + sl * KV_LD_SLOT + 256 * wave, (uint32_t)(t * KV_BQ + lane) * 4);
   };
 
   // Per-lane LDS offsets, tile-relative:
@@ -245,7 +254,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       for (int e = 0; e < 2; ++e) troff[mb][e] = tile_off8(tr_row + 8 * e, dim >> 3, (dim >> 2) & 1);
     }
   }
-  const int vrow = 64 * wave * kRowBytes;  // this wave's rows of the V block
+  // This wave's rows of the V block (a multiple of 256: the chunk XOR below
+  // only touches bits 5..7).
+  const int vrow = KV_V_OFF + 64 * wave * kRowBytes;
 
   f32x16 dka[2][4], dva[2][4];
 #pragma unroll
@@ -278,7 +289,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // tro: transpose-read lane offsets (troff, passed through opaque() by the
   // caller outside the region the products are scheduled in).
   auto dvdk = [&](int psl, const int (&tro)[4][2]) {
-    const int qsl = kRing + psl * KV_SLOT, osl = qsl + KV_TILE;
+    const int qsl = psl * KV_SLOT, osl = qsl + KV_TILE;
     bf16x8 a_do[2], a_q[2];
     auto rdt = [&](int n, int b) {
       const int mb = n >> 1, ro2 = 16 * (n & 1) * kRowBytes;
@@ -301,9 +312,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   auto step = [&](int t, auto bc) {
     constexpr int sl = decltype(bc)::value;
     constexpr int psl = (sl + KV_NSLOT - 1) % KV_NSLOT;  // slot of tile t - 1
-    constexpr int qsl = kRing + sl * KV_SLOT;            // smem offsets of this slot's parts
+    constexpr int qsl = sl * KV_SLOT;                    // smem offsets of this slot's parts
     constexpr int osl = qsl + KV_TILE;
-    constexpr int lsl = qsl + 2 * KV_TILE;
+    constexpr int lsl = KV_LD_OFF + sl * KV_LD_SLOT;
     constexpr int dsl = lsl + 256;
     // Tile t has landed once only tile t + 1's loads may be in flight; the
     // barrier then publishes every wave's part of it and frees the slot that
@@ -380,7 +391,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     // one element per MFMA; sched_barrier keeps the compiler to that order.
     const float* lb = reinterpret_cast<const float*>(smem + lsl);
     const float* db = reinterpret_cast<const float*>(smem + dsl);
-    const int pq = kRing + psl * KV_SLOT, po = pq + KV_TILE;
+    const int pq = psl * KV_SLOT, po = pq + KV_TILE;
     bf16x8 npb[2][2], nsb[2][2];
     bf16x8 a_do[2], a_q[2];
     f32x4 l4[2], d4[2];
@@ -437,8 +448,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
   // Slot 3 feeds the first step's dV / dK products: clear it.
   {
-    char* z = smem + kRing + 3 * KV_SLOT;
-    for (int o = tid * 16; o < 2 * KV_TILE; o += KV_THREADS * 16) lds_write16(z, o, u32x4{0u, 0u, 0u, 0u});
+    char* z = smem + 3 * KV_SLOT;
+    for (int o = tid * 16; o < KV_SLOT; o += KV_THREADS * 16) lds_write16(z, o, u32x4{0u, 0u, 0u, 0u});
   }
   issue_tile(t0, 0);
   issue_tile(t0 + 1, 1);
@@ -505,6 +516,7 @@ constexpr int DQ_SLOT = 2 * DQ_TILE;                  // K tile, then V tile
 constexpr int DQ_NSLOT = 4;
 constexpr int DQ_SMEM = DQ_NSLOT * DQ_SLOT;           // 64 KiB
 constexpr int DQ_LOADS_PER_TILE = 2 * DQ_TLOADS;
+constexpr int DQ_AHEAD = 3;                           // LDS read-ahead of phases A and B, in k-steps
 
 // S^T / dP^T MFMA with the B operand (Q^T or dO^T) in AGPRs and the result in
 // VGPRs; hazards as for mfma_v (s_fence2 after the last one).
@@ -698,15 +710,20 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const char* kb = smem + SL * DQ_SLOT;
     const char* vb = kb + DQ_TILE;
 
-    // Phase A: S^T for both query groups, K fragments one step ahead.
+    // Phase A: S^T for both query groups.  K and V fragments are read
+    // DQ_AHEAD k-steps before their MFMAs (two MFMAs per step are too short
+    // to cover the LDS latency); V's first ones during the last K steps.
     f32x16 s[2], dp[2];
-    bf16x8 ka[2], va[2];
-    ka[0] = __builtin_bit_cast(bf16x8, lds_read16(kb, roff[0]));
+    bf16x8 ka[DQ_AHEAD + 1], va[DQ_AHEAD + 1];
+#pragma unroll
+    for (int j = 0; j < DQ_AHEAD; ++j) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(kb, roff[j]));
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
-      const int b = kc & 1;
-      if (kc < 7) ka[b ^ 1] = __builtin_bit_cast(bf16x8, lds_read16(kb, roff[kc + 1]));
-      if (kc == 6) va[0] = __builtin_bit_cast(bf16x8, lds_read16(vb, roff[0]));
+      const int b = kc % (DQ_AHEAD + 1);
+      if (kc + DQ_AHEAD < 8)
+        ka[(kc + DQ_AHEAD) % (DQ_AHEAD + 1)] = __builtin_bit_cast(bf16x8, lds_read16(kb, roff[kc + DQ_AHEAD]));
+      else
+        va[kc + DQ_AHEAD - 8] = __builtin_bit_cast(bf16x8, lds_read16(vb, roff[kc + DQ_AHEAD - 8]));
       if (kc == 0) {
         mfma_va0(s[0], ka[b], qf[0][kc]);
         mfma_va0(s[1], ka[b], qf[1][kc]);
@@ -723,8 +740,9 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
-      const int b = kc & 1;
-      if (kc < 7) va[b ^ 1] = __builtin_bit_cast(bf16x8, lds_read16(vb, roff[kc + 1]));
+      const int b = kc % (DQ_AHEAD + 1);
+      if (kc + DQ_AHEAD < 8)
+        va[(kc + DQ_AHEAD) % (DQ_AHEAD + 1)] = __builtin_bit_cast(bf16x8, lds_read16(vb, roff[kc + DQ_AHEAD]));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
