@@ -175,7 +175,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
   // Causal: the first key blocks see the most queries; issue them first.
   int kb, bh;
-  block_head(blockIdx.x, (N + KV_BK - 1) / KV_BK, BH, false, &kb, &bh);
+  block_head(blockIdx.x, (N + KV_BK - 1) / KV_BK, BH, false, CAUSAL, &kb, &bh);
   const int k0 = kb * KV_BK;
   const int kw = k0 + 64 * wave;
 
@@ -556,7 +556,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
   // Causal: issue the longest query blocks first.
   int qblk, bh;
-  block_head(blockIdx.x, nqb, BH, CAUSAL, &qblk, &bh);
+  block_head(blockIdx.x, nqb, BH, CAUSAL, CAUSAL, &qblk, &bh);
   const int q0 = qblk * DQ_BQ;
   const int q0w = q0 + DQ_QW * wave;
 

@@ -124,18 +124,32 @@ __device__ __forceinline__ void buf_load16_lds(rsrc_t r, char* lds_base, uint32_
 }
 
 // Workgroup -> (block, head) map.  Workgroups are dealt round-robin to the 8
-// XCDs (each with its own L2), so when the head count is a multiple of 8 the
-// blocks of one head are given to one XCD and issued together there: the
-// head's K/V (or Q/dO) stream is then shared through that XCD's L2.  Within a
-// head, blocks go in the order `rev` asks for (longest causal work first).
+// XCDs (each with its own L2); when the head count is a multiple of 8, every
+// head's blocks go to one XCD, so the head's K/V (or Q/dO) stream is shared
+// through that XCD's L2.  Within an XCD the order is either head by head
+// (`lpt` false: a head's blocks run together, the best L2 reuse when all
+// blocks cost the same) or block rank by block rank across the XCD's heads
+// (`lpt` true: causal blocks differ in cost up to the sequence length over the
+// block size, and issuing every head's longest block before any shorter one
+// keeps the last workgroups short; head by head, a head issued late puts its
+// longest block at the end, which idled about a third of the machine with two
+// workgroups per CU).  `rev` reverses the block index (the longest causal
+// block is the last query block, but the first key block).
 constexpr int kXcds = 8;
-__device__ __forceinline__ void block_head(int id, int nblk, int BH, bool rev, int* blk, int* bh) {
+__device__ __forceinline__ void block_head(int id, int nblk, int BH, bool rev, bool lpt, int* blk,
+                                           int* bh) {
   int b, hd;
   if ((BH % kXcds) == 0) {
     const int xcd = id % kXcds;
     const int local = id / kXcds;
-    hd = xcd + kXcds * (local / nblk);
-    b = local % nblk;
+    const int hpx = BH / kXcds;  // heads per XCD
+    if (lpt) {
+      hd = xcd + kXcds * (local % hpx);
+      b = local / hpx;
+    } else {
+      hd = xcd + kXcds * (local / nblk);
+      b = local % nblk;
+    }
   } else {
     hd = id % BH;
     b = id / BH;

@@ -65,7 +65,7 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
   // Causal: issue the longest query blocks first.
   int qb, bh;
-  block_head(blockIdx.x, nqb, BH, CAUSAL, &qb, &bh);
+  block_head(blockIdx.x, nqb, BH, CAUSAL, CAUSAL, &qb, &bh);
   const int q0 = qb * FWD_BR;
   const int q0w = q0 + wave * FWD_QW;
   const int qrow = q0w + col;
