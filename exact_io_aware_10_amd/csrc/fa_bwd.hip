@@ -754,6 +754,9 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         const int sg = idx >> 4, si = idx & 15;
         s[sg][si] = fast_exp2(__builtin_fmaf(s[sg][si], sl2, -l2[sg]));
         s[sg][si + 1] = fast_exp2(__builtin_fmaf(s[sg][si + 1], sl2, -l2[sg]));
+        // Here, between this MFMA and the next, not bunched after the last
+        // one (where the compiler otherwise puts them).
+        asm volatile("" : "+v"(s[sg][si]), "+v"(s[sg][si + 1]));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
