@@ -72,3 +72,30 @@ def make_workload(name: str, with_do: bool | None = None) -> dict:
     if with_do is None:
         with_do = w["bwd"]
     return make(w["B"], w["H"], w["N"], w["seed"], w["qk_std"], with_do)
+
+
+def rotation_signs(seed: int, d: int = HEAD_DIM) -> np.ndarray:
+    """The FP8 path's random sign vector (float32 entries +-1), drawn here so
+    that the oracle and the GPU receive the same one."""
+    rng = np.random.default_rng(seed)
+    return np.where(rng.random(d) < 0.5, -1.0, 1.0).astype(np.float32)
+
+
+FP8_SIGN_SEED = 9000
+
+
+def make_outlier(B: int, H: int, N: int, seed: int, amp: float, channels=(3, 40, 77, 120)) -> dict:
+    """Q, K, V (bf16 bits) where a few head dimensions of K and V are `amp`
+    times larger than the rest (the outlier features that incoherent
+    processing is meant for), and Q is divided by sqrt(amp) to keep the scores
+    in a moderate range."""
+    x = make(B, H, N, seed)
+    out = {}
+    for name, factor in (("q", None), ("k", amp), ("v", amp)):
+        f = bf16_bits_to_f64(x[name])
+        if factor is None:
+            f = f / np.sqrt(amp)
+        else:
+            f[..., list(channels)] *= factor
+        out[name] = f32_to_bf16_bits(f.astype(np.float32))
+    return out
