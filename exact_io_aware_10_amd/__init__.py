@@ -12,8 +12,12 @@ Functions mirror the C entry points:
   fa_bwd_dkdv(q, k, v, dO, ws, dk, dv, scale, causal)          -> None
   fa_bwd_dq(q, k, v, dO, ws, dq, scale, causal)                -> None
   fa_bwd_workspace_size(B, H, N, d, causal)                    -> int
+  fa_fp8_codes_size(B, H, N, d, layout), fa_fp8_exps_size(B, H, N, d) -> int
+  fa_fp8_quantize(x, signs, codes, exps, layout)               -> None
+  fa_fwd_fp8(q8, qe, k8, ke, v8, ve, signs, o, lse, scale, causal) -> None
   fa_strerror(status)                                          -> str
-plus allocating conveniences forward(...) and backward(...).
+plus allocating conveniences forward(...), backward(...), quantize_fp8(...)
+and forward_fp8(...).
 """
 from __future__ import annotations
 
@@ -61,6 +65,14 @@ def load_library() -> ctypes.CDLL:
         lib.fa_bwd_dkdv.restype = i
         lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, f, i, vp]
         lib.fa_bwd_dq.restype = i
+        lib.fa_fp8_codes_size.argtypes = [i, i, i, i, i]
+        lib.fa_fp8_codes_size.restype = sz
+        lib.fa_fp8_exps_size.argtypes = [i, i, i, i]
+        lib.fa_fp8_exps_size.restype = sz
+        lib.fa_fp8_quantize.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
+        lib.fa_fp8_quantize.restype = i
+        lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_fwd_fp8.restype = i
         lib.fa_strerror.argtypes = [i]
         lib.fa_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -194,3 +206,80 @@ def backward(q, k, v, o, do, lse, scale: float, causal: bool, stream=None, works
         workspace = workspace_for(B, H, N, causal, q.device)
     fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale, causal, workspace, stream)
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# FP8 path
+# ---------------------------------------------------------------------------
+FA_FP8_ROWS = 0
+FA_FP8_VT = 1
+
+
+def fa_fp8_codes_size(B: int, H: int, N: int, d: int = HEAD_DIM, layout: int = FA_FP8_ROWS) -> int:
+    return int(load_library().fa_fp8_codes_size(B, H, N, d, int(layout)))
+
+
+def fa_fp8_exps_size(B: int, H: int, N: int, d: int = HEAD_DIM) -> int:
+    return int(load_library().fa_fp8_exps_size(B, H, N, d))
+
+
+def _check_buf(name, t, dtype, nbytes):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous ROCm device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} needs at least {nbytes} bytes")
+
+
+def fa_fp8_quantize(x, signs, codes, exps, layout: int, stream=None) -> None:
+    B, H, N, d = _shape(x)
+    _check_tensor("x", x, torch.bfloat16, (B, H, N, d))
+    _check_tensor("signs", signs, torch.float32, (d,))
+    _check_buf("codes", codes, torch.uint8, fa_fp8_codes_size(B, H, N, d, layout))
+    _check_buf("exps", exps, torch.int32, fa_fp8_exps_size(B, H, N, d))
+    st = load_library().fa_fp8_quantize(_ptr(x), _ptr(signs), _ptr(codes), _ptr(exps), B, H, N, d,
+                                        int(layout), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st)
+
+
+def fa_fwd_fp8(q8, qe, k8, ke, v8, ve, signs, o, lse, scale: float, causal: bool,
+               stream=None) -> None:
+    B, H, N, d = _shape(o)
+    _check_tensor("o", o, torch.bfloat16, (B, H, N, d))
+    _check_tensor("lse", lse, torch.float32, (B, H, N))
+    _check_tensor("signs", signs, torch.float32, (d,))
+    rows = fa_fp8_codes_size(B, H, N, d, FA_FP8_ROWS)
+    _check_buf("q8", q8, torch.uint8, rows)
+    _check_buf("k8", k8, torch.uint8, rows)
+    _check_buf("v8", v8, torch.uint8, fa_fp8_codes_size(B, H, N, d, FA_FP8_VT))
+    ne = fa_fp8_exps_size(B, H, N, d)
+    for name, t in (("qe", qe), ("ke", ke), ("ve", ve)):
+        _check_buf(name, t, torch.int32, ne)
+    st = load_library().fa_fwd_fp8(_ptr(q8), _ptr(qe), _ptr(k8), _ptr(ke), _ptr(v8), _ptr(ve),
+                                   _ptr(signs), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                                   int(bool(causal)), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st)
+
+
+def quantize_fp8(x, signs, layout: int, stream=None):
+    """Allocate and fill (codes, exps) for one tensor."""
+    B, H, N, d = _shape(x)
+    codes = torch.empty(max(fa_fp8_codes_size(B, H, N, d, layout), 16), dtype=torch.uint8, device=x.device)
+    exps = torch.empty(max(fa_fp8_exps_size(B, H, N, d) // 4, 4), dtype=torch.int32, device=x.device)
+    fa_fp8_quantize(x, signs, codes, exps, layout, stream)
+    return codes, exps
+
+
+def forward_fp8(q, k, v, signs, scale: float, causal: bool, stream=None):
+    """Quantise Q, K, V and run the FP8 forward.  Returns (o, lse)."""
+    B, H, N, d = _shape(q)
+    q8, qe = quantize_fp8(q, signs, FA_FP8_ROWS, stream)
+    k8, ke = quantize_fp8(k, signs, FA_FP8_ROWS, stream)
+    v8, ve = quantize_fp8(v, signs, FA_FP8_VT, stream)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd_fp8(q8, qe, k8, ke, v8, ve, signs, o, lse, scale, causal, stream)
+    return o, lse

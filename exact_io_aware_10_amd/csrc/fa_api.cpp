@@ -127,6 +127,49 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_fp8_codes_size(int B, int H, int N, int d, int layout) {
+  bool empty = false;
+  if (check_common(B, H, N, d, 1.f, 0, &empty) != FA_OK || empty) return 0;
+  if (layout == FA_FP8_ROWS) return (size_t)B * H * N * d;
+  if (layout == FA_FP8_VT) return (size_t)B * H * ((N + 63) / 64) * 64 * d;
+  return 0;
+}
+
+size_t fa_fp8_exps_size(int B, int H, int N, int d) {
+  bool empty = false;
+  if (check_common(B, H, N, d, 1.f, 0, &empty) != FA_OK || empty) return 0;
+  return (size_t)B * H * ((N + 63) / 64) * sizeof(int);
+}
+
+int fa_fp8_quantize(const void* x, const float* signs, void* codes, int* exps, int B, int H, int N,
+                    int d, int layout, void* stream) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, 1.f, 0, &empty);
+  if (st != FA_OK || empty) return st;
+  if (layout != FA_FP8_ROWS && layout != FA_FP8_VT) return FA_ERR_INVALID_ARG;
+  if (!x || !signs || !codes || !exps) return FA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(signs) || !aligned16(codes) || !aligned16(exps))
+    return FA_ERR_UNSUPPORTED;
+  hipError_t e = fa::launch_fp8_quant(x, signs, codes, exps, B, H, N, layout,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_fp8(const void* q8, const int* qexp, const void* k8, const int* kexp, const void* v8,
+               const int* vexp, const float* signs, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, void* stream) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, causal, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!q8 || !qexp || !k8 || !kexp || !v8 || !vexp || !signs || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q8) || !aligned16(qexp) || !aligned16(k8) || !aligned16(kexp) || !aligned16(v8) ||
+      !aligned16(vexp) || !aligned16(signs) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_UNSUPPORTED;
+  hipError_t e = fa::launch_fwd_fp8(q8, qexp, k8, kexp, v8, vexp, signs, o, lse, B, H, N, scale,
+                                    causal, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "success";

@@ -22,4 +22,11 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          const float* ws, void* dq, int B, int H, int N, float scale, int causal,
                          hipStream_t stream);
 
+// FP8 path (fa_fp8.hip).
+hipError_t launch_fp8_quant(const void* x, const float* signs, void* codes, int* exps, int B, int H,
+                            int N, int layout, hipStream_t stream);
+hipError_t launch_fwd_fp8(const void* q8, const int* qexp, const void* k8, const int* kexp,
+                          const void* v8, const int* vexp, const float* signs, void* o, float* lse,
+                          int B, int H, int N, float scale, int causal, hipStream_t stream);
+
 }  // namespace fa

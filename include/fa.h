@@ -116,6 +116,51 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
               const void* workspace, size_t workspace_bytes, void* dq,
               int B, int H, int N, int d, float scale, int causal, void* stream);
 
+/*
+ * FP8 forward with incoherent processing ("Interrogating the GPU, part 5:
+ * FlashAttention", section "What did FlashAttention-3 do with Hopper?": keys
+ * and values quantised per block after a random Hadamard rotation, which
+ * spreads outliers across the block; "FlashAttention versions", section
+ * "FlashAttention-3": block-level quantisation with incoherent processing).
+ * An approximation of the forward above, with its own accuracy contract.
+ *
+ * With sigma a sign vector chosen by the caller (d float32 entries, each +1
+ * or -1) and H the d x d Sylvester Hadamard matrix:
+ *   X' = (X o sigma) H for X = Q, K, V, computed in float32 as a fast
+ *   Walsh-Hadamard transform (stage s = 0..6 pairs entries i and i + 2^s,
+ *   bit s of i clear, into (a + b, a - b));
+ *   each block of 64 consecutive rows of a head (the last block may be
+ *   shorter) gets the exponent e, the smallest integer with
+ *   max|X'| <= 448 * 2^e (-127 for an all-zero block), and the codes
+ *   E4M3(X' * 2^-e): OCP FP8 E4M3, round to nearest even;
+ *   the forward then uses S = (scale / d) Q' K'^T, P rounded to E4M3 for the
+ *   P V' product, and O = ((P V') H / d) o sigma.
+ *
+ * fa_fp8_quantize: x [B,H,N,d] bf16 -> codes and exps.
+ *   layout FA_FP8_ROWS (0): codes [B,H,N,d] uint8, row-major (Q and K);
+ *   layout FA_FP8_VT (1): codes [B,H,ceil(N/64),d,64] uint8: per 64-key tile,
+ *     one 64-byte row per dimension; inside a row, block-local key r sits at
+ *     32*((r>>2)&1) + 16*(r>>5) + 4*((r>>3)&3) + (r&3); keys past N are zero
+ *     (V).
+ *   exps: [B,H,ceil(N/64)] int32 block exponents.  signs: d float32 values,
+ *   device memory.  fa_fp8_codes_size / fa_fp8_exps_size give the byte sizes
+ *   (0 for invalid or empty sizes).
+ * fa_fwd_fp8: q8 and k8 in FA_FP8_ROWS layout, v8 in FA_FP8_VT layout, with
+ *   their exps and the same signs; o [B,H,N,d] bf16 and lse [B,H,N] float32
+ *   as for fa_fwd (lse of the scores the FP8 path computes).
+ * Accuracy (unit-variance inputs, d = 128): O within about 0.1 and LSE within
+ * about 0.1 of exact attention; the E4M3 rounding of P dominates.  Shapes,
+ * alignment, scale, causal, stream and error codes as for fa_fwd.
+ */
+enum { FA_FP8_ROWS = 0, FA_FP8_VT = 1 };
+size_t fa_fp8_codes_size(int B, int H, int N, int d, int layout);
+size_t fa_fp8_exps_size(int B, int H, int N, int d);
+int fa_fp8_quantize(const void* x, const float* signs, void* codes, int* exps,
+                    int B, int H, int N, int d, int layout, void* stream);
+int fa_fwd_fp8(const void* q8, const int* qexp, const void* k8, const int* kexp,
+               const void* v8, const int* vexp, const float* signs, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, void* stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_strerror(int status);
 

@@ -115,3 +115,31 @@ def test_binding_requires_device_tensors(fa):
     t = torch.zeros((1, 1, 4, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.forward(t, t, t, 0.1, False)
+
+
+def test_fp8_sizes(fa):
+    assert fa.fa_fp8_codes_size(1, 2, 100, 128, fa.FA_FP8_ROWS) == 2 * 100 * 128
+    assert fa.fa_fp8_codes_size(1, 2, 100, 128, fa.FA_FP8_VT) == 2 * 128 * 128  # 2 tiles of 64 keys
+    assert fa.fa_fp8_codes_size(1, 2, 100, 128, 7) == 0
+    assert fa.fa_fp8_codes_size(1, 2, 100, 96, fa.FA_FP8_ROWS) == 0
+    assert fa.fa_fp8_exps_size(2, 3, 65, 128) == 2 * 3 * 2 * 4
+    assert fa.fa_fp8_exps_size(0, 3, 65, 128) == 0
+
+
+def test_fp8_entry_points_reject_bad_arguments(fa):
+    lib = fa.load_library()
+    assert lib.fa_fp8_quantize(FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 128, 2, None) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fp8_quantize(FAKE, None, FAKE, FAKE, 1, 1, 16, 128, 0, None) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fp8_quantize(FAKE, FAKE, FAKE + 4, FAKE, 1, 1, 16, 128, 0, None) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_fp8_quantize(FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 64, 0, None) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_fp8_quantize(None, None, None, None, 1, 0, 16, 128, 0, None) == fa.FA_OK
+    p = [FAKE] * 9
+    assert lib.fa_fwd_fp8(*p, 1, 1, 16, 128, 0.1, 3, None) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_fp8(*p, 1, 1, 16, 128, float("nan"), 0, None) == fa.FA_ERR_INVALID_ARG
+    for i in range(9):
+        q = list(p)
+        q[i] = None
+        assert lib.fa_fwd_fp8(*q, 1, 1, 16, 128, 0.1, 0, None) == fa.FA_ERR_INVALID_ARG
+        q[i] = FAKE + 8
+        assert lib.fa_fwd_fp8(*q, 1, 1, 16, 128, 0.1, 0, None) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_fwd_fp8(*([None] * 9), 1, 1, 0, 128, 0.1, 0, None) == fa.FA_OK

@@ -1,0 +1,179 @@
+"""GPU parity of the FP8 path (fa_fp8_quantize, fa_fwd_fp8) against the FP8
+oracle (oracle/fp8.py), through the C ABI.
+
+* Quantisation: the codes and block exponents are integer results, compared
+  bit for bit with the oracle's (both sides rotate in float32 in the same
+  butterfly order, so both round the same values to E4M3).
+* Forward: O and LSE against the oracle's float64 emulation of the same FP8
+  computation (same codes, E4M3 P against the same reference maxima).  LSE
+  within the bf16 path's bar.  O within the bf16 path's bar plus the final
+  bf16 rounding (2^-8 |O|), with one allowance: the GPU forms P in float32,
+  so a P that lies within a few float32 ulps of an E4M3 rounding boundary can
+  round to the neighbouring code on one side only (about one score in 10^5
+  to 10^6), moving O_ic by up to 2^-3 P_ij |V_jc|; every element must stay
+  within the bar plus 2^-3 max_j P_ij max_j |V_jc|, and at least 99.9 % of
+  them within the bar itself.  And against exact attention within the FP8
+  path's error budget (E4M3 keeps 3 mantissa bits).
+"""
+import numpy as np
+import pytest
+
+import fa_inputs
+from oracle import attention as ora
+from oracle import fp8 as ofp8
+from tests.gpu_helpers import TOL_LSE, TOL_OUT, f64, from_dev, max_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NS = [1, 17, 63, 64, 65, 129, 300, 1000]
+TOL_FP8_EXACT_O = 0.2      # FP8 path against exact attention, unit-variance inputs
+TOL_FP8_EXACT_LSE = 0.15
+
+
+def _p_rowmax(q, k, causal):
+    """max_j P_ij of exact attention, one head ([N, d] float64), by row blocks."""
+    N = q.shape[0]
+    out = np.empty(N)
+    keys = np.arange(N)
+    for r0 in range(0, N, 1024):
+        rows = np.arange(r0, min(N, r0 + 1024))
+        s = fa_inputs.SCALE * (q[rows] @ k.T)
+        if causal:
+            s[rows[:, None] < keys[None, :]] = -np.inf
+        mx = s.max(axis=1)
+        out[rows] = 1.0 / np.exp(s - mx[:, None]).sum(axis=1)
+    return out
+
+
+def _check_o(o, emu, q, k, v, causal, label):
+    """O against the emulation under the bar described in the module docstring."""
+    bar = TOL_OUT + 2.0 ** -8 * np.abs(emu)
+    err = np.abs(o - emu)
+    B, H = o.shape[:2]
+    flip = np.empty_like(err)
+    for b in range(B):
+        for hh in range(H):
+            pm = _p_rowmax(q[b, hh], k[b, hh], causal)
+            vm = np.abs(v[b, hh]).max(axis=0)
+            flip[b, hh] = 2.0 ** -3 * pm[:, None] * vm[None, :]
+    within = float(np.mean(err <= bar))
+    worst = float((err - bar - flip).max())
+    print(f"{label}: O vs FP8 oracle max {err.max():.2e}, {100 * within:.4f} % within the bar, "
+          f"worst excess over bar + one flip {worst:.2e}", flush=True)
+    assert worst <= 0 and within >= 0.999
+
+
+@pytest.fixture(scope="module")
+def fa():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_io_aware_10_amd as fa
+    fa.load_library()
+    return fa
+
+
+def _signs(torch):
+    return torch.from_numpy(fa_inputs.rotation_signs(fa_inputs.FP8_SIGN_SEED)).cuda()
+
+
+def _vt_pos(r):
+    # key order inside a transposed V tile row, as include/fa.h documents it
+    return 32 * ((r >> 2) & 1) + 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3)
+
+
+def _check_codes(fa, torch, bits, layout, label):
+    B, H, N, d = bits.shape
+    x = to_dev(bits, torch)
+    codes, exps = fa.quantize_fp8(x, _signs(torch), layout)
+    torch.cuda.synchronize()
+    want_c, want_e = ofp8.quantize_tensor(f64(bits), fa_inputs.rotation_signs(fa_inputs.FP8_SIGN_SEED))
+    nb = (N + 63) // 64
+    got_e = exps.cpu().numpy()[:B * H * nb].reshape(B, H, nb)
+    assert np.array_equal(got_e, want_e), f"{label}: block exponents differ"
+    c = codes.cpu().numpy()
+    if layout == fa.FA_FP8_ROWS:
+        got = c[:B * H * N * d].reshape(B, H, N, d)
+        bad = np.argwhere(got != want_c)
+        assert bad.size == 0, f"{label}: {len(bad)} codes differ, first at {bad[:3].tolist()}"
+    else:
+        t = c[:B * H * nb * 64 * d].reshape(B, H, nb, d, 64)
+        pos = np.array([_vt_pos(r) for r in range(64)])
+        got = t[:, :, :, :, pos].transpose(0, 1, 2, 4, 3).reshape(B, H, nb * 64, d)
+        assert np.array_equal(got[:, :, :N], want_c), f"{label}: transposed codes differ"
+        assert np.all((got[:, :, N:] & 0x7F) == 0), f"{label}: padding keys are not zero"
+    print(f"{label}: codes and exponents bit-exact", flush=True)
+
+
+@pytest.mark.parametrize("N", NS)
+@pytest.mark.parametrize("layout", [0, 1])
+def test_quantize_bit_exact(fa, N, layout):
+    import torch
+    x = fa_inputs.make(1, 3, N, seed=8100 + N)
+    _check_codes(fa, torch, x["v" if layout else "k"], layout, f"quantize N={N} layout={layout}")
+
+
+def test_quantize_bit_exact_outliers_and_zero_rows(fa):
+    import torch
+    x = fa_inputs.make_outlier(2, 2, 200, seed=8200, amp=20.0)
+    for layout, name in ((0, "k"), (1, "v")):
+        _check_codes(fa, torch, x[name], layout, f"quantize outliers layout={layout}")
+    z = np.zeros((1, 1, 70, 128), dtype=np.uint16)  # an all-zero head: exponent -127, zero codes
+    _check_codes(fa, torch, z, 0, "quantize zeros")
+
+
+def _run_fp8(fa, torch, x, causal):
+    q, k, v = (to_dev(x[n], torch) for n in "qkv")
+    o, lse = fa.forward_fp8(q, k, v, _signs(torch), fa_inputs.SCALE, causal)
+    torch.cuda.synchronize()
+    return from_dev(o), from_dev(lse)
+
+
+@pytest.mark.parametrize("N", NS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_fp8_small(fa, N, causal):
+    import torch
+    x = fa_inputs.make(1, 2, N, seed=8300 + N + 7 * causal)
+    o, lse = _run_fp8(fa, torch, x, causal)
+    q, k, v = (f64(x[n]) for n in "qkv")
+    sg = fa_inputs.rotation_signs(fa_inputs.FP8_SIGN_SEED)
+    eo_, el_ = ofp8.forward_emulated(q, k, v, sg, fa_inputs.SCALE, causal)
+    xo, xl = ora.forward(q, k, v, fa_inputs.SCALE, causal)
+    l1 = max_err(lse, el_)
+    e2, l2 = max_err(o, xo), max_err(lse, xl)
+    print(f"fp8 N={N} causal={causal}: vs FP8 oracle LSE {l1:.2e}; "
+          f"vs exact O {e2:.2e} LSE {l2:.2e}", flush=True)
+    _check_o(o, eo_, q, k, v, causal, f"fp8 N={N} causal={causal}")
+    assert l1 <= TOL_LSE
+    assert e2 <= TOL_FP8_EXACT_O and l2 <= TOL_FP8_EXACT_LSE
+
+
+def test_forward_fp8_outliers(fa):
+    import torch
+    x = fa_inputs.make_outlier(1, 2, 512, seed=8400, amp=20.0)
+    o, lse = _run_fp8(fa, torch, x, True)
+    q, k, v = (f64(x[n]) for n in "qkv")
+    sg = fa_inputs.rotation_signs(fa_inputs.FP8_SIGN_SEED)
+    eo_, el_ = ofp8.forward_emulated(q, k, v, sg, fa_inputs.SCALE, True)
+    l1 = max_err(lse, el_)
+    print(f"fp8 outliers: vs FP8 oracle LSE {l1:.2e} (max |O| {np.abs(eo_).max():.1f})", flush=True)
+    _check_o(o, eo_, q, k, v, True, "fp8 outliers")
+    assert l1 <= TOL_LSE
+
+
+def test_forward_fp8_full_size_two_heads(fa):
+    """B1 H64 N8192 causal in the launch configuration the benchmark times;
+    two whole heads checked against the emulation (it takes seconds per head)."""
+    import torch
+    w = fa_inputs.WORKLOADS["causal_b1_h64_n8192"]
+    x = fa_inputs.make_workload("causal_b1_h64_n8192", with_do=False)
+    o, lse = _run_fp8(fa, torch, x, True)
+    sg = fa_inputs.rotation_signs(fa_inputs.FP8_SIGN_SEED)
+    for hh in (0, 37):
+        q, k, v = (f64(x[n][:, hh:hh + 1]) for n in "qkv")
+        eo_, el_ = ofp8.forward_emulated(q, k, v, sg, fa_inputs.SCALE, True)
+        l1 = max_err(lse[:, hh:hh + 1], el_)
+        print(f"fp8 {w['N']} head {hh}: vs FP8 oracle LSE {l1:.2e}", flush=True)
+        _check_o(o[:, hh:hh + 1], eo_, q, k, v, True, f"fp8 {w['N']} head {hh}")
+        assert l1 <= TOL_LSE
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
