@@ -123,6 +123,37 @@ __device__ __forceinline__ void buf_load16_lds(rsrc_t r, char* lds_base, uint32_
                                            voff, 0, 0, 0);
 }
 
+// LDS-direct loads written as inline assembly, invisible to the compiler's
+// LDS dependency tracking: kernels that use them order the ring themselves
+// (ring_wait_barrier).  M0 carries the wave-uniform LDS base; nothing else in
+// these kernels uses M0.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+// lds_base: wave-uniform LDS byte address (lds_addr of the destination);
+// 16 (dma16) or 4 (dma4) bytes per lane, lane i writing lds_base + size i.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(r)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(r)
+               : "memory");
+}
+// Wait until at most PENDING of this wave's LDS-direct loads are in flight
+// and its LDS reads are done, then barrier.  The "memory" clobber keeps the
+// compiler from moving LDS accesses across it.
+template <int PENDING>
+__device__ __forceinline__ void ring_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(PENDING) : "memory");
+}
+__device__ __forceinline__ void dma_drain() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
+
 // Workgroup -> (block, head) map.  Workgroups are dealt round-robin to the 8
 // XCDs (each with its own L2); when the head count is a multiple of 8, every
 // head's blocks go to one XCD, so the head's K/V (or Q/dO) stream is shared

@@ -165,8 +165,11 @@ __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c, int scale_
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, 127);
 }
 
+// Three workgroups per CU (one wave of each per SIMD, at most 168 VGPRs and
+// 32 KiB of LDS apiece): a third wave per SIMD keeps the matrix pipe fed
+// while the other two exponentiate, which two waves do not.
 template <bool CAUSAL>
-__global__ __launch_bounds__(F8_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(F8_THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const int* __restrict__ qexp,
                     const uint8_t* __restrict__ k8, const int* __restrict__ kexp,
                     const uint8_t* __restrict__ v8, const int* __restrict__ vexp,
