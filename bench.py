@@ -30,7 +30,7 @@ import fa_inputs  # noqa: E402
 from exact_io_aware_10_amd import accounting as acc  # noqa: E402
 
 METRIC = "attention fwd/bwd TFLOP/s at d=128 bf16, % of MI355X dense bf16 MFMA peak"
-KERNEL_FILES = ("fa_device.hpp", "fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp", "fa_internal.h")
+KERNEL_FILES = ("fa_device.hpp", "fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip", "fa_api.cpp", "fa_internal.h")
 
 
 def log(*a):
@@ -93,6 +93,60 @@ def cpu_baseline(x, w, heads: int):
     }
 
 
+def fp8_forward(fa, torch, q, k, v, w, workload, stream, warmup: int, steps: int):
+    """The FP8 forward (incoherent processing) on the same Q, K, V: rotate and
+    quantise Q, K, V (three launches), then FP8 attention.  Timed apart from
+    the bf16 step with HIP events on the launch stream; FLOPs are credited
+    as for the bf16 forward (4 N^2 d per head, halved when causal)."""
+    B, H, N, causal = w["B"], w["H"], w["N"], w["causal"]
+    d = fa_inputs.HEAD_DIM
+    signs = torch.from_numpy(fa_inputs.rotation_signs(fa_inputs.FP8_SIGN_SEED)).to(q.device)
+    bufs = {}
+    for name, x, layout in (("q", q, fa.FA_FP8_ROWS), ("k", k, fa.FA_FP8_ROWS), ("v", v, fa.FA_FP8_VT)):
+        codes = torch.empty(fa.fa_fp8_codes_size(B, H, N, d, layout), dtype=torch.uint8, device=q.device)
+        exps = torch.empty(fa.fa_fp8_exps_size(B, H, N, d) // 4, dtype=torch.int32, device=q.device)
+        bufs[name] = (x, codes, exps, layout)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+
+    def run(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        for x, codes, exps, layout in bufs.values():
+            fa.fa_fp8_quantize(x, signs, codes, exps, layout, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.fa_fwd_fp8(bufs["q"][1], bufs["q"][2], bufs["k"][1], bufs["k"][2], bufs["v"][1],
+                      bufs["v"][2], signs, o, lse, fa_inputs.SCALE, causal, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for s in range(steps):
+        run(evs[s])
+    torch.cuda.synchronize()
+    quant_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    flops = acc.fwd_flops(B, H, N, d, causal)
+    attn_tf = flops / (attn_ms * 1e-3) / 1e12
+    return {
+        "dtype": "fp8 e4m3 (Q, K, V, P), fp32 accumulate, bf16 O",
+        "quantize_ms": quant_ms,
+        "quantize_hbm_gbps": 3 * acc.fp8_quant_bytes(B, H, N, d) / (quant_ms * 1e-3) / 1e9,
+        "attn_ms": attn_ms,
+        "attn_tflops": attn_tf,
+        "attn_frac_of_fp8_peak": attn_tf / acc.MI355X_FP8_DENSE_TFLOPS,
+        "attn_frac_of_bf16_peak": attn_tf / acc.MI355X_BF16_DENSE_TFLOPS,
+        "attn_traffic": traffic_for("fwd_fp8", workload),
+        "attn_algorithmic_bytes": acc.fp8_fwd_bytes(B, H, N, d),
+        "with_quantize_tflops": flops / ((attn_ms + quant_ms) * 1e-3) / 1e12,
+        "fp8_peak_tflops": acc.MI355X_FP8_DENSE_TFLOPS,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +156,7 @@ def main():
     ap.add_argument("--workload", default="causal_b1_h64_n8192", choices=sorted(fa_inputs.WORKLOADS))
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle timing sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward timing")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -229,6 +284,12 @@ def main():
     roof["work"] = what
     roof["avg_launch_ms"] = kern_ms[dom]
 
+    fp8 = None
+    if not args.no_fp8:
+        fp8 = fp8_forward(fa, torch, q, k, v, w, args.workload, stream, args.warmup, args.steps)
+        log(f"fp8 forward: quantise {fp8['quantize_ms']:.3f} ms, attention {fp8['attn_ms']:.3f} ms "
+            f"({fp8['attn_tflops']:.0f} TFLOP/s credited)")
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"timing the fp64 oracle on {args.cpu_heads} heads ...")
@@ -254,6 +315,7 @@ def main():
         "peak_tflops": peak,
         **out_extra,
         "roofline": roof,
+        "fp8_forward": fp8,
         "cpu_baseline": cpu,
         "source_hash": source_hash(),
     }

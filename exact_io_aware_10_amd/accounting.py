@@ -9,6 +9,7 @@ remove the traffic?").
 """
 from __future__ import annotations
 
+FP8 = 1
 BF16 = 2
 FP32 = 4
 
@@ -42,6 +43,18 @@ def bwd_pre_bytes(B: int, H: int, N: int, d: int) -> float:
     return float(B * H * (2 * N * d * BF16 + 3 * N * FP32))
 
 
+def fp8_quant_bytes(B: int, H: int, N: int, d: int) -> float:
+    """Rotate and quantise one tensor: read it in bf16, write one E4M3 byte
+    per element and one int32 exponent per 64-row block."""
+    return float(B * H * (N * d * (BF16 + FP8) + -(-N // 64) * FP32))
+
+
+def fp8_fwd_bytes(B: int, H: int, N: int, d: int) -> float:
+    """FP8 attention: read the Q, K, V codes and their block exponents, write
+    O (bf16) and LSE (fp32)."""
+    return float(B * H * (3 * N * d * FP8 + 3 * -(-N // 64) * FP32 + N * d * BF16 + N * FP32))
+
+
 def naive_intensity(N: int, d: int) -> float:
     """Textbook three-kernel attention: 4 N^2 d FLOPs over 8 N^2 + 8 N d bytes
     ("Interrogating the GPU, part 5", textbook section, intensity equation)."""
@@ -55,4 +68,5 @@ def flash_intensity(N: int, d: int) -> float:
 
 # MI355X published peaks used as roofline denominators.
 MI355X_BF16_DENSE_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz
+MI355X_FP8_DENSE_TFLOPS = 5033.2    # 256 CU x 8192 FLOP/clk x 2.4 GHz
 MI355X_HBM_GBPS = 8000.0

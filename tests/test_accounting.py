@@ -56,3 +56,11 @@ def test_metric_conventions():
     assert acc.bwd_flops(1, 64, 8192, 128, True) == pytest.approx(2.7488e12, rel=1e-4)
     assert acc.fwd_bytes(1, 64, 8192, 128) == 64 * (8 * 8192 * 128 + 4 * 8192)
     assert acc.bwd_bytes(2, 16, 4096, 128) == 32 * (16 * 4096 * 128 + 12 * 4096)
+
+
+def test_fp8_byte_counts():
+    # One E4M3 byte per element, an int32 exponent per 64-row block (65 rows
+    # -> 2 blocks); the attention writes the same bf16 O and fp32 LSE.
+    assert acc.fp8_quant_bytes(1, 1, 65, 128) == 65 * 128 * 3 + 2 * 4
+    assert acc.fp8_fwd_bytes(1, 1, 64, 128) == 3 * 64 * 128 + 3 * 4 + 64 * 128 * 2 + 64 * 4
+    assert acc.MI355X_FP8_DENSE_TFLOPS == pytest.approx(2 * acc.MI355X_BF16_DENSE_TFLOPS)
