@@ -6,7 +6,16 @@ oracle (oracle/fp8.py), through the C ABI.
   butterfly order, so both round the same values to E4M3).
 * Forward: O and LSE against the oracle's float64 emulation of the same FP8
   computation (same codes, E4M3 P against the same reference maxima).  LSE
-  within the bf16 path's bar.  O within the bf16 path's bar plus the final
+  within the bf16 path's bar plus the FP8 MFMA's accumulation error: the
+  matrix cores do not sum the 64 exact products of one instruction in full
+  float32 -- measured on random E4M3 operands, the result is off the exact
+  sum by up to 2.2e-4 of sum_k |a_k b_k| (about 2^-12) -- so a score
+  s_ij = (scale / 128) Q'_i . K'_j (two chained instructions) may be off by
+  2^-11 (scale / 128) sum_k |Q'_ik K'_jk|, and LSE_i, a P-weighted mean of its
+  scores' errors, by at most the largest of these over the row's visible
+  keys.  That bound is a worst case (about 5e-3 at unit variance); on
+  unit-variance inputs the errors stay far below it and the bf16 path's bar
+  itself is required as well.  O within the bf16 path's bar plus the final
   bf16 rounding (2^-8 |O|), with one allowance: the GPU forms P in float32,
   so a P that lies within a few float32 ulps of an E4M3 rounding boundary can
   round to the neighbouring code on one side only (about one score in 10^5
@@ -43,6 +52,38 @@ def _p_rowmax(q, k, causal):
         mx = s.max(axis=1)
         out[rows] = 1.0 / np.exp(s - mx[:, None]).sum(axis=1)
     return out
+
+
+def _lse_bar(q, k, causal):
+    """Per-row LSE bar against the emulation: TOL_LSE plus the FP8 MFMA
+    accumulation allowance described in the module docstring, from the
+    dequantised rotated Q' and K' of the oracle."""
+    sg = fa_inputs.rotation_signs(fa_inputs.FP8_SIGN_SEED)
+    qc, qe = ofp8.quantize_tensor(q, sg)
+    kc, ke = ofp8.quantize_tensor(k, sg)
+    B, H, N, d = q.shape
+    bar = np.empty((B, H, N))
+    for b in range(B):
+        for hh in range(H):
+            qa = np.abs(ofp8.e4m3_decode(qc[b, hh])) * np.exp2(np.repeat(qe[b, hh], 64)[:N])[:, None]
+            ka = np.abs(ofp8.e4m3_decode(kc[b, hh])) * np.exp2(np.repeat(ke[b, hh], 64)[:N])[:, None]
+            for r0 in range(0, N, 2048):
+                rows = np.arange(r0, min(N, r0 + 2048))
+                m = qa[rows] @ ka.T
+                if causal:
+                    m[rows[:, None] < np.arange(N)[None, :]] = 0.0
+                bar[b, hh, rows] = m.max(axis=1)
+    return TOL_LSE + 2.0 ** -11 * fa_inputs.SCALE / d * bar
+
+
+def _check_lse(lse, emu, q, k, causal, label, unit_variance=True):
+    err = np.abs(lse - emu)
+    bar = _lse_bar(q, k, causal)
+    print(f"{label}: LSE vs FP8 oracle max {err.max():.2e} (bar {bar.min():.2e} .. {bar.max():.2e})",
+          flush=True)
+    assert np.all(err <= bar)
+    if unit_variance:
+        assert err.max() <= TOL_LSE
 
 
 def _check_o(o, emu, q, k, v, causal, label):
@@ -139,13 +180,29 @@ def test_forward_fp8_small(fa, N, causal):
     sg = fa_inputs.rotation_signs(fa_inputs.FP8_SIGN_SEED)
     eo_, el_ = ofp8.forward_emulated(q, k, v, sg, fa_inputs.SCALE, causal)
     xo, xl = ora.forward(q, k, v, fa_inputs.SCALE, causal)
-    l1 = max_err(lse, el_)
     e2, l2 = max_err(o, xo), max_err(lse, xl)
-    print(f"fp8 N={N} causal={causal}: vs FP8 oracle LSE {l1:.2e}; "
-          f"vs exact O {e2:.2e} LSE {l2:.2e}", flush=True)
+    print(f"fp8 N={N} causal={causal}: vs exact O {e2:.2e} LSE {l2:.2e}", flush=True)
     _check_o(o, eo_, q, k, v, causal, f"fp8 N={N} causal={causal}")
-    assert l1 <= TOL_LSE
+    _check_lse(lse, el_, q, k, causal, f"fp8 N={N} causal={causal}")
     assert e2 <= TOL_FP8_EXACT_O and l2 <= TOL_FP8_EXACT_LSE
+
+
+@pytest.mark.parametrize("N", [300, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_fp8_large_scores(fa, N, causal):
+    """Q, K with standard deviation 4 (scaled scores of standard deviation 16,
+    as in the long-sequence workload): far outside the FP8 path's accuracy
+    contract against exact attention (E4M3 rounding of Q' and K' moves such
+    scores by about one unit), but the kernel must still match the emulation
+    of the same FP8 arithmetic: large maxima, frequent rescales."""
+    import torch
+    x = fa_inputs.make(1, 2, N, seed=8500 + N + causal, qk_std=4.0)
+    o, lse = _run_fp8(fa, torch, x, causal)
+    q, k, v = (f64(x[n]) for n in "qkv")
+    sg = fa_inputs.rotation_signs(fa_inputs.FP8_SIGN_SEED)
+    eo_, el_ = ofp8.forward_emulated(q, k, v, sg, fa_inputs.SCALE, causal)
+    _check_o(o, eo_, q, k, v, causal, f"fp8 std 4 N={N} causal={causal}")
+    _check_lse(lse, el_, q, k, causal, f"fp8 std 4 N={N} causal={causal}", unit_variance=False)
 
 
 def test_forward_fp8_outliers(fa):
@@ -155,10 +212,9 @@ def test_forward_fp8_outliers(fa):
     q, k, v = (f64(x[n]) for n in "qkv")
     sg = fa_inputs.rotation_signs(fa_inputs.FP8_SIGN_SEED)
     eo_, el_ = ofp8.forward_emulated(q, k, v, sg, fa_inputs.SCALE, True)
-    l1 = max_err(lse, el_)
-    print(f"fp8 outliers: vs FP8 oracle LSE {l1:.2e} (max |O| {np.abs(eo_).max():.1f})", flush=True)
+    print(f"fp8 outliers: max |O| {np.abs(eo_).max():.1f}", flush=True)
     _check_o(o, eo_, q, k, v, True, "fp8 outliers")
-    assert l1 <= TOL_LSE
+    _check_lse(lse, el_, q, k, True, "fp8 outliers")
 
 
 def test_forward_fp8_full_size_two_heads(fa):
@@ -172,8 +228,6 @@ def test_forward_fp8_full_size_two_heads(fa):
     for hh in (0, 37):
         q, k, v = (f64(x[n][:, hh:hh + 1]) for n in "qkv")
         eo_, el_ = ofp8.forward_emulated(q, k, v, sg, fa_inputs.SCALE, True)
-        l1 = max_err(lse[:, hh:hh + 1], el_)
-        print(f"fp8 {w['N']} head {hh}: vs FP8 oracle LSE {l1:.2e}", flush=True)
         _check_o(o[:, hh:hh + 1], eo_, q, k, v, True, f"fp8 {w['N']} head {hh}")
-        assert l1 <= TOL_LSE
+        _check_lse(lse[:, hh:hh + 1], el_, q, k, True, f"fp8 {w['N']} head {hh}")
     assert np.isfinite(o).all() and np.isfinite(lse).all()
