@@ -50,6 +50,19 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, float scale, int causal, void* stream) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, causal, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_UNSUPPORTED;
+  hipError_t e = fa::launch_fwd_split(q, k, v, o, lse, B, H, N, scale, causal,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal) {
   bool empty = false;
   if (check_common(B, H, N, d, 1.f, causal, &empty) != FA_OK) return 0;

@@ -257,8 +257,260 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 }
 
-hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                      int H, int N, float scale, int causal, hipStream_t stream) {
+// ---------------------------------------------------------------------------
+// Key-split forward, for grids too small to occupy the chip.
+// ---------------------------------------------------------------------------
+// With few (batch, head) pairs and a short sequence, one workgroup per 128
+// query rows leaves most CUs idle and each wave walks every key tile in turn,
+// waiting on memory at each ("Interrogating the GPU, part 5", FlashAttention-2
+// section: batch x heads alone does not fill the GPU).  Here a workgroup owns
+// 32 query rows and its 4 waves split the keys: wave w takes the 32-key tiles
+// w, w + 4, w + 8, ... into LDS of its own (double-buffered, no barrier in the
+// loop) and keeps its own online-softmax state (m_w, l_w, O_w).  At the end
+// the four partial states merge by the rescale rule of the online softmax:
+//   M = max_w m_w,  L = sum_w 2^(m_w - M) l_w,
+//   O = sum_w 2^(m_w - M) O_w / L,  LSE = ln2 (M + log2 L),
+// through LDS, each wave producing 32 of the 128 output dimensions.
+constexpr int SPL_QW = 32;                         // query rows per workgroup
+constexpr int SPL_WAVES = 4;
+constexpr int SPL_BC = 32;                         // keys per tile
+constexpr int SPL_TILE = SPL_BC * kRowBytes;       // 8 KiB (K or V)
+constexpr int SPL_WAVE_LDS = 4 * SPL_TILE;         // [buffer][K | V] per wave
+constexpr int SPL_SMEM = SPL_WAVES * SPL_WAVE_LDS;  // 128 KiB
+constexpr int SPL_LOADS = SPL_TILE / 1024;         // 1 KiB LDS-direct loads per tile and tensor
+constexpr int SPL_PART = 64 * 16;                  // floats in one O^T block (64 lanes x 16)
+static_assert((SPL_WAVES * SPL_WAVES * SPL_PART + 2 * SPL_WAVES * SPL_QW) * 4 <= SPL_SMEM,
+              "the merge buffers must fit the tile buffers they reuse");
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(SPL_WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                      const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
+                      float* __restrict__ lse, int BH, int N, int nqb, float sl2) {
+  __shared__ __attribute__((aligned(16))) char smem[SPL_SMEM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int col = lane & 31;
+
+  int qb, bh;
+  block_head(blockIdx.x, nqb, BH, CAUSAL, CAUSAL, &qb, &bh);
+  const int q0 = qb * SPL_QW;
+  const int qrow = q0 + col;
+
+  const size_t head = (size_t)bh * (size_t)N * kD;
+  const uint32_t head_bytes = (uint32_t)N * kRowBytes;
+  const rsrc_t rq = make_rsrc(q + head, head_bytes);
+  const rsrc_t rk = make_rsrc(k + head, head_bytes);
+  const rsrc_t rv = make_rsrc(v + head, head_bytes);
+
+  bf16x8 qf[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc)
+    qf[kc] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)qrow * kRowBytes + (2 * kc + h) * 16));
+
+  const int kend = CAUSAL ? min(N, q0 + SPL_QW) : N;
+  const int ntiles = (kend + SPL_BC - 1) / SPL_BC;
+  const int nmine = ntiles > wave ? (ntiles - wave + SPL_WAVES - 1) / SPL_WAVES : 0;
+
+  // This wave's LDS: buffer b holds K at b * 2 * SPL_TILE and V after it.
+  char* const wlds = smem + wave * SPL_WAVE_LDS;
+  const uint32_t wlds_addr = lds_addr(wlds);
+  // Load n of a tile fills rows 4 n .. 4 n + 3 (1 KiB, lane-linear); lane i
+  // lands on physical chunk i % 16 of its row and fetches the logical chunk
+  // the swizzle stores there.  Rows past N read as zero.
+  uint32_t ld_voff[SPL_LOADS];
+#pragma unroll
+  for (int n = 0; n < SPL_LOADS; ++n) {
+    const int row = 4 * n + (lane >> 4);
+    ld_voff[n] = (uint32_t)row * kRowBytes + (((lane & 15) ^ swz(row)) << 4);
+  }
+  auto issue = [&](int j, int b) {
+    const uint32_t toff = (uint32_t)(wave + SPL_WAVES * j) * SPL_TILE;
+    const uint32_t kb = wlds_addr + b * 2 * SPL_TILE;
+#pragma unroll
+    for (int n = 0; n < SPL_LOADS; ++n) {
+      dma16(rk, kb + 1024 * n, ld_voff[n] + toff);
+      dma16(rv, kb + SPL_TILE + 1024 * n, ld_voff[n] + toff);
+    }
+  };
+
+  int koff[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) koff[kc] = tile_off(col, 2 * kc + h);
+  int voff[4][2];
+  {
+    const int tr_s = lane & 15;
+    const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (tr_s & 3);
+    const int tr_row = 4 * h + (tr_s >> 2);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int dim = 32 * mb + tr_dim;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) voff[mb][e] = tile_off8(tr_row + 8 * e, dim >> 3, (dim >> 2) & 1);
+    }
+  }
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
+  float m = -INFINITY;
+  float l = 0.f;
+
+  if (nmine > 0) issue(0, 0);
+  for (int j = 0; j < nmine; ++j) {
+    const int b = j & 1;
+    // Tile j + 1 goes into the other buffer, whose reads (tile j - 1) are
+    // complete; then wait for tile j alone.
+    if (j + 1 < nmine) {
+      issue(j + 1, b ^ 1);
+      asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * SPL_LOADS) : "memory");
+    } else {
+      dma_drain();
+    }
+    const char* kb = wlds + b * 2 * SPL_TILE;
+    const char* vb = kb + SPL_TILE;
+    const int k0 = (wave + SPL_WAVES * j) * SPL_BC;
+
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc)
+      s = mfma32(__builtin_bit_cast(bf16x8, lds_read16(kb, koff[kc])), qf[kc], s);
+
+    if ((CAUSAL && k0 + SPL_BC - 1 > q0) || k0 + SPL_BC > N) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (key >= N || (CAUSAL && key > qrow)) s[i] = -INFINITY;
+      }
+    }
+
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = halves_max(mx);
+    const float mcand = mx * sl2;
+    if (__builtin_amdgcn_ballot_w64(mcand > m + kTau) != 0) {
+      const float mnew = fmaxf(m, mcand);
+      const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m - mnew);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mb][i] *= alpha;
+    }
+    const float mu = (m == -INFINITY) ? 0.f : m;
+    float rs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(__builtin_fmaf(s[i], sl2, -mu));
+      s[i] = p;
+      rs += p;
+    }
+    l += rs;
+
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const bf16x8 pb = pack8(s[8 * u], s[8 * u + 1], s[8 * u + 2], s[8 * u + 3], s[8 * u + 4],
+                              s[8 * u + 5], s[8 * u + 6], s[8 * u + 7]);
+      const char* rb = vb + 16 * u * kRowBytes;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        acc[mb] = mfma32(join(lds_read_tr(rb + voff[mb][0]), lds_read_tr(rb + voff[mb][1])), pb, acc[mb]);
+    }
+  }
+
+  // Merge.  Every wave's reads and loads are done before the tile buffers
+  // are reused: part[w][mb] holds wave w's O^T block mb (element group g of
+  // lane x at float4 index 64 g + x), stats[w] its m and row sum per query.
+  const float lt = halves_sum(l);
+  __syncthreads();
+  float* part = reinterpret_cast<float*>(smem);
+  float* stats = part + SPL_WAVES * SPL_WAVES * SPL_PART;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 w4 = {acc[mb][4 * g], acc[mb][4 * g + 1], acc[mb][4 * g + 2], acc[mb][4 * g + 3]};
+      *reinterpret_cast<f32x4*>(part + (wave * SPL_WAVES + mb) * SPL_PART + 4 * (64 * g + lane)) = w4;
+    }
+  if (h == 0) {
+    stats[(2 * wave) * SPL_QW + col] = m;
+    stats[(2 * wave + 1) * SPL_QW + col] = lt;
+  }
+  __syncthreads();
+
+  float mw[SPL_WAVES], M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < SPL_WAVES; ++w) {
+    mw[w] = stats[(2 * w) * SPL_QW + col];
+    M = fmaxf(M, mw[w]);
+  }
+  float L = 0.f, cw[SPL_WAVES];
+#pragma unroll
+  for (int w = 0; w < SPL_WAVES; ++w) {
+    cw[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);  // a wave without keys adds nothing
+    L += cw[w] * stats[(2 * w + 1) * SPL_QW + col];
+  }
+  const float inv = 1.f / L;
+  // This wave writes output dimensions 32 wave .. 32 wave + 31 (block mb = wave).
+  f32x16 ob;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ob[i] = 0.f;
+#pragma unroll
+  for (int w = 0; w < SPL_WAVES; ++w)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 x4 = *reinterpret_cast<const f32x4*>(part + (w * SPL_WAVES + wave) * SPL_PART +
+                                                       4 * (64 * g + lane));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ob[4 * g + e] += cw[w] * x4[e];
+    }
+  if (qrow < N) {
+    char* orow = reinterpret_cast<char*>(o + head) + (size_t)qrow * kRowBytes;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int i = 4 * g;
+      u32x2 w2 = {pack_bf16(ob[i] * inv, ob[i + 1] * inv), pack_bf16(ob[i + 2] * inv, ob[i + 3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + (32 * wave + 8 * g + 4 * h) * 2) = w2;
+    }
+    if (wave == 0 && h == 0) lse[(size_t)bh * N + qrow] = (M + __log2f(L)) * kLn2;
+  }
+}
+
+// Below these row-block grid sizes the key-split kernel runs (measured on
+// small shapes: it is 1.5-1.9x faster up to 64 row-block workgroups, and up to
+// 128 when causal, where the row blocks also differ in length; from 128
+// non-causal or 256 causal workgroups the row-block kernel is faster).
+constexpr int kSplitBelow = 128;
+constexpr int kSplitBelowCausal = 256;
+
+hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int N, float scale, int causal, hipStream_t stream) {
+  const int BH = B * H;
+  const int nqb = (N + SPL_QW - 1) / SPL_QW;
+  const float sl2 = scale * kLog2e;
+  dim3 grid((unsigned)(nqb * BH)), block(SPL_WAVES * 64);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  uint16_t* oo = static_cast<uint16_t*>(o);
+  if (causal)
+    hipLaunchKernelGGL(fwd_split_kernel<true>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2);
+  else
+    hipLaunchKernelGGL(fwd_split_kernel<false>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_rows(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int N, float scale, int causal, hipStream_t stream) {
   const int BH = B * H;
   const int nqb = (N + FWD_BR - 1) / FWD_BR;
   const float sl2 = scale * kLog2e;
@@ -272,6 +524,14 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
   else
     hipLaunchKernelGGL(fwd_kernel<false>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int N, float scale, int causal, hipStream_t stream) {
+  const long rows_grid = (long)B * H * ((N + FWD_BR - 1) / FWD_BR);
+  if (rows_grid < (causal ? kSplitBelowCausal : kSplitBelow))
+    return launch_fwd_split(q, k, v, o, lse, B, H, N, scale, causal, stream);
+  return launch_fwd_rows(q, k, v, o, lse, B, H, N, scale, causal, stream);
 }
 
 }  // namespace fa

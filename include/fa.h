@@ -64,6 +64,22 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
+ * The forward pass through its key-split kernel, whatever the sizes.  fa_fwd
+ * runs it by itself when B * H * ceil(N / 128) is below 128 (below 256 when
+ * causal), i.e. when one workgroup per 128 query rows leaves most of the
+ * GPU's 256 CUs idle (few heads and a short sequence; "Interrogating the GPU,
+ * part 5", FlashAttention-2 section: batch x heads alone does not fill the
+ * GPU).  A workgroup then owns 32 query
+ * rows and its four wavefronts each run the online softmax over a quarter of
+ * the key tiles; the four partial results are merged with the same rescale
+ * rule the online softmax uses between tiles.  Arguments, outputs and error
+ * behaviour exactly as for fa_fwd; exported so that either kernel can be
+ * tested and timed on any sizes.
+ */
+int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
  * Bytes of device workspace the backward pass needs for these sizes:
  * 2*B*H*N float32 (rounded up to 256 bytes), laid out as [D | L*log2(e)],
  * with D_i = sum_k dO_ik O_ik and L the forward's log-sum-exp.  Returns 0

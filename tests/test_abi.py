@@ -27,8 +27,8 @@ def fa():
 
 def test_header_declares_the_boundary():
     names = declared()
-    for n in ("fa_fwd", "fa_bwd", "fa_bwd_workspace_size", "fa_strerror", "fa_bwd_preprocess",
-              "fa_bwd_dkdv", "fa_bwd_dq"):
+    for n in ("fa_fwd", "fa_fwd_split", "fa_bwd", "fa_bwd_workspace_size", "fa_strerror",
+              "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"):
         assert n in names
 
 
@@ -72,21 +72,24 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
 def test_fwd_rejects_bad_arguments(fa, args, expect):
     B, H, N, d, scale, causal, mis = args
     lib = fa.load_library()
-    assert lib.fa_fwd(FAKE + mis, FAKE, FAKE, FAKE, FAKE, B, H, N, d, scale, causal, None) == expect
+    for entry in (lib.fa_fwd, lib.fa_fwd_split):
+        assert entry(FAKE + mis, FAKE, FAKE, FAKE, FAKE, B, H, N, d, scale, causal, None) == expect
 
 
 def test_fwd_rejects_null_pointers(fa):
     lib = fa.load_library()
-    for i in range(5):
-        ptrs = [FAKE] * 5
-        ptrs[i] = None
-        assert lib.fa_fwd(*ptrs, 1, 1, 16, 128, 0.1, 0, None) == fa.FA_ERR_INVALID_ARG
+    for entry in (lib.fa_fwd, lib.fa_fwd_split):
+        for i in range(5):
+            ptrs = [FAKE] * 5
+            ptrs[i] = None
+            assert entry(*ptrs, 1, 1, 16, 128, 0.1, 0, None) == fa.FA_ERR_INVALID_ARG
 
 
 def test_empty_problem_is_a_no_op(fa):
     lib = fa.load_library()
     assert lib.fa_fwd(None, None, None, None, None, 0, 4, 16, 128, 0.1, 0, None) == fa.FA_OK
     assert lib.fa_fwd(None, None, None, None, None, 1, 1, 0, 128, 0.1, 1, None) == fa.FA_OK
+    assert lib.fa_fwd_split(None, None, None, None, None, 1, 1, 0, 128, 0.1, 1, None) == fa.FA_OK
     assert lib.fa_bwd(*([None] * 9), 1, 0, 16, 128, 0.1, 0, None, 0, None) == fa.FA_OK
 
 

@@ -107,6 +107,33 @@ def test_fwd_causal_b1_h8_n32768_std4(fa):
     assert eo <= TOL_OUT and el <= TOL_LSE
 
 
+def test_fwd_split_entry_at_full_sizes(fa):
+    """The key-split kernel (fa_fwd_split) on two workloads fa_fwd gives to
+    the row-block kernel: whole heads and sampled rows of every head."""
+    import torch
+    for name, heads in (("causal_b2_h16_n4096", [(1, 9)]), ("fwd_b4_h32_n2048", [(2, 5)])):
+        w = fa_inputs.WORKLOADS[name]
+        x = fa_inputs.make_workload(name, with_do=False)
+        q, k, v = (to_dev(x[n], torch) for n in "qkv")
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        fa.fa_fwd_split(q, k, v, o, lse, fa_inputs.SCALE, w["causal"])
+        torch.cuda.synchronize()
+        O, L = from_dev(o), from_dev(lse)
+        assert np.isfinite(O).all() and np.isfinite(L).all()
+        worst = [0.0, 0.0]
+        for b, hh in heads:
+            sl = (slice(b, b + 1), slice(hh, hh + 1))
+            ro, rl = ora.forward(f64(x["q"][sl]), f64(x["k"][sl]), f64(x["v"][sl]), fa_inputs.SCALE,
+                                 w["causal"])
+            worst = [max(worst[0], max_err(O[sl], ro)), max(worst[1], max_err(L[sl], rl))]
+        eo, el = check_rows(w, x, O, L, [(b, hh) for b in range(w["B"]) for hh in range(w["H"])],
+                            sample_rows(w["N"], 12, 9))
+        log(f"{name} through fa_fwd_split: whole heads O {worst[0]:.2e} LSE {worst[1]:.2e}; "
+            f"sampled rows O {eo:.2e} LSE {el:.2e}")
+        assert max(worst[0], eo) <= TOL_OUT and max(worst[1], el) <= TOL_LSE
+
+
 def _backward_check(fa, name, heads):
     import torch
     w = fa_inputs.WORKLOADS[name]

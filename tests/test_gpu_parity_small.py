@@ -42,6 +42,38 @@ def test_forward_small(fa, N, causal, BH):
     assert eo <= TOL_OUT and el <= TOL_LSE
 
 
+def _forward_vs_oracle(fa, entry, B, H, N, causal, seed, label):
+    import torch
+    x = fa_inputs.make(B, H, N, seed=seed)
+    scale = fa_inputs.SCALE
+    q, k, v = (to_dev(x[n], torch) for n in "qkv")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    entry(q, k, v, o, lse, scale, causal)
+    torch.cuda.synchronize()
+    ro, rl = ora.forward(f64(x["q"]), f64(x["k"]), f64(x["v"]), scale, causal)
+    eo, el = max_err(from_dev(o), ro), max_err(from_dev(lse), rl)
+    print(f"{label} N={N} causal={causal} B{B} H{H}: O err {eo:.2e} LSE err {el:.2e}", flush=True)
+    assert eo <= TOL_OUT and el <= TOL_LSE
+
+
+# fa_fwd takes the key-split kernel while B * H * ceil(N / 128) < 128 (< 256
+# when causal): every shape above; 256 heads put it on the row-block kernel
+# at any N.
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 129, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_row_kernel_small(fa, N, causal):
+    _forward_vs_oracle(fa, fa.fa_fwd, 2, 128, N, causal, 7500 + N + 100 * causal, "fwd rows")
+
+
+# The key-split kernel through its own entry point on a grid fa_fwd would
+# give to the row-block kernel (many heads, XCD-mapped).
+@pytest.mark.parametrize("N", [1, 33, 65, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_split_entry_many_heads(fa, N, causal):
+    _forward_vs_oracle(fa, fa.fa_fwd_split, 2, 128, N, causal, 7700 + N + 100 * causal, "fwd split")
+
+
 @pytest.mark.parametrize("N", NS)
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("BH", [(1, 1), (1, 3)])
