@@ -157,6 +157,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle timing sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward timing")
+    ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
+                    help="time the K steps as one HIP graph replay (auto: for forward-only "
+                         "workloads, whose microsecond kernels would otherwise wait on the host)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -228,16 +231,39 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    use_graph = args.graph == "on" or (args.graph == "auto" and not with_bwd)
+    if use_graph:
+        # The K steps captured once and replayed: the GPU runs them back to
+        # back with no host launch work in between.  Kernel time = replay
+        # time / K (events on the stream the replay is launched on).
+        graph = torch.cuda.CUDAGraph()
+        gstream = torch.cuda.Stream()
+        with torch.cuda.stream(gstream):
+            with torch.cuda.graph(graph, stream=gstream):
+                for _ in range(args.steps):
+                    fa.fa_fwd(q, k, v, o, lse, scale, causal)
+        graph.replay()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        graph.replay()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern_ms = {"fwd": ev[0].elapsed_time(ev[1]) / args.steps}
+    else:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            step(evs[s])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
     ms_per_step = wall / args.steps * 1e3
-    kern_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; per kernel (ms): "
         + ", ".join(f"{n} {t:.3f}" for n, t in kern_ms.items()))
 
@@ -248,6 +274,7 @@ def main():
     value = step_f / (ms_per_step * 1e-3) / 1e12
     fwd_tf = fwd_f / (kern_ms["fwd"] * 1e-3) / 1e12
     out_extra = {
+        "timing": "one HIP graph of the K steps" if use_graph else "HIP events around every kernel",
         "fwd_ms": kern_ms["fwd"],
         "fwd_tflops": fwd_tf,
         "fwd_frac_of_peak": fwd_tf / peak,
