@@ -201,6 +201,36 @@ def test_non_default_stream(fa):
     assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)
 
 
+@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_split"])
+def test_graph_replays_match_eager(fa, entry):
+    """The forward captured in a HIP graph (as bench.py times the forward-only
+    workloads): every replay, with eager work and synchronisations between
+    them, equals the eager result bit for bit (the kernels are deterministic)."""
+    import torch
+    B, H, N = 2, 128, 300  # fa_fwd takes the row-block kernel at this size
+    x = fa_inputs.make(B, H, N, seed=9960)
+    q, k, v = (to_dev(x[n], torch) for n in "qkv")
+    run = getattr(fa, entry)
+    ref_o, ref_l = torch.empty_like(q), torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    run(q, k, v, ref_o, ref_l, SCALE, True)
+    o, lse = torch.empty_like(q), torch.empty_like(ref_l)
+    graph = torch.cuda.CUDAGraph()
+    gs = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(graph, stream=gs):
+            run(q, k, v, o, lse, SCALE, True)
+    for i in range(3):
+        o.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_l), f"replay {i}"
+        run(q, k, v, ref_o, ref_l, SCALE, True)  # eager work between the replays
+        torch.cuda.synchronize()
+
+
 def test_error_paths_with_device_tensors(fa):
     import torch
     N = 64
