@@ -217,6 +217,31 @@ def test_forward_fp8_outliers(fa):
     _check_lse(lse, el_, q, k, True, "fp8 outliers")
 
 
+def test_forward_fp8_non_causal_full_size(fa):
+    """B4 H32 N2048 non-causal: two heads against the emulation, all heads
+    finite and within the FP8 path's budget against exact attention on
+    sampled rows."""
+    import torch
+    x = fa_inputs.make_workload("fwd_b4_h32_n2048", with_do=False)
+    o, lse = _run_fp8(fa, torch, x, False)
+    sg = fa_inputs.rotation_signs(fa_inputs.FP8_SIGN_SEED)
+    for b, hh in ((0, 0), (3, 29)):
+        q, k, v = (f64(x[n][b:b + 1, hh:hh + 1]) for n in "qkv")
+        eo_, el_ = ofp8.forward_emulated(q, k, v, sg, fa_inputs.SCALE, False)
+        _check_o(o[b:b + 1, hh:hh + 1], eo_, q, k, v, False, f"fp8 B4 H32 N2048 head {(b, hh)}")
+        _check_lse(lse[b:b + 1, hh:hh + 1], el_, q, k, False, f"fp8 B4 H32 N2048 head {(b, hh)}")
+    rows = np.arange(0, 2048, 97)
+    worst = [0.0, 0.0]
+    Q, K, V = (f64(x[n]) for n in "qkv")
+    for b in range(4):
+        for hh in range(0, 32, 5):
+            xo, xl = ora.row_sample_forward(Q, K, V, fa_inputs.SCALE, False, b, hh, rows)
+            worst = [max(worst[0], max_err(o[b, hh, rows], xo)), max(worst[1], max_err(lse[b, hh, rows], xl))]
+    print(f"fp8 B4 H32 N2048 vs exact on sampled rows: O {worst[0]:.2e} LSE {worst[1]:.2e}", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    assert worst[0] <= TOL_FP8_EXACT_O and worst[1] <= TOL_FP8_EXACT_LSE
+
+
 def test_forward_fp8_full_size_two_heads(fa):
     """B1 H64 N8192 causal in the launch configuration the benchmark times;
     two whole heads checked against the emulation (it takes seconds per head)."""
