@@ -33,34 +33,33 @@ int check_common(int B, int H, int N, int d, float scale, int causal, bool* empt
   return FA_OK;
 }
 
+// Argument checks shared by the forward entry points, then the launch.
+typedef hipError_t (*fwd_launcher)(const void*, const void*, const void*, void*, float*, int, int,
+                                   int, float, int, hipStream_t);
+int checked_fwd(fwd_launcher launch, const void* q, const void* k, const void* v, void* o,
+                float* lse, int B, int H, int N, int d, float scale, int causal, void* stream) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, causal, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_UNSUPPORTED;
+  hipError_t e = launch(q, k, v, o, lse, B, H, N, scale, causal, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
            int d, float scale, int causal, void* stream) {
-  bool empty = false;
-  int st = check_common(B, H, N, d, scale, causal, &empty);
-  if (st != FA_OK || empty) return st;
-  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-    return FA_ERR_UNSUPPORTED;
-  hipError_t e = fa::launch_fwd(q, k, v, o, lse, B, H, N, scale, causal,
-                                static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return checked_fwd(fa::launch_fwd, q, k, v, o, lse, B, H, N, d, scale, causal, stream);
 }
 
 int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N, int d, float scale, int causal, void* stream) {
-  bool empty = false;
-  int st = check_common(B, H, N, d, scale, causal, &empty);
-  if (st != FA_OK || empty) return st;
-  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-    return FA_ERR_UNSUPPORTED;
-  hipError_t e = fa::launch_fwd_split(q, k, v, o, lse, B, H, N, scale, causal,
-                                      static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return checked_fwd(fa::launch_fwd_split, q, k, v, o, lse, B, H, N, d, scale, causal, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal) {
