@@ -146,3 +146,18 @@ def test_fp8_entry_points_reject_bad_arguments(fa):
         q[i] = FAKE + 8
         assert lib.fa_fwd_fp8(*q, 1, 1, 16, 128, 0.1, 0, None) == fa.FA_ERR_UNSUPPORTED
     assert lib.fa_fwd_fp8(*([None] * 9), 1, 1, 0, 128, 0.1, 0, None) == fa.FA_OK
+
+
+def test_missing_library_fails_loudly():
+    """No fallback: with the library absent, the binding raises instead of
+    computing anything another way."""
+    import subprocess
+    import sys
+    code = ("import exact_io_aware_10_amd as fa\n"
+            "fa.LIB_PATH = '/nonexistent/libfa.so'\n"
+            "try:\n"
+            "    fa.load_library()\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0 and "raised:" in r.stdout and "missing" in r.stdout
