@@ -34,12 +34,18 @@ import numpy as np
 __all__ = ["forward", "backward", "online_forward", "row_sample_forward"]
 
 
-def _check(q, k, v):
+def _check(q, k, v, causal):
+    """q [B, H, Nq, d], k and v [B, H, Nk, d].  Nq may differ from Nk only
+    without the causal mask (a query row attends to every key, as in [P3]'s
+    worked example, which streams one query over eight keys); the causal mask
+    is defined for equal lengths."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    if q.ndim != 4 or q.shape != k.shape or k.shape != v.shape:
-        raise ValueError("q, k, v must share shape [B, H, N, d]")
+    if q.ndim != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    if causal and q.shape[2] != k.shape[2]:
+        raise ValueError("the causal mask needs as many queries as keys")
     return q, k, v
 
 
@@ -67,9 +73,9 @@ def forward(q, k, v, scale, causal, row_block=2048):
     Rows are independent, so they are processed `row_block` at a time only to
     bound memory; no sum is split.
 
-    Returns (O [B,H,N,d] float64, LSE [B,H,N] float64).
+    Returns (O [B,H,Nq,d] float64, LSE [B,H,Nq] float64).
     """
-    q, k, v = _check(q, k, v)
+    q, k, v = _check(q, k, v, causal)
     B, H, N, d = q.shape
     o = np.empty_like(q)
     lse = np.empty((B, H, N), dtype=np.float64)
@@ -116,7 +122,9 @@ def backward(q, k, v, o, do, scale, causal):
 
     Returns (dQ, dK, dV [B,H,N,d], D [B,H,N]) in float64.
     """
-    q, k, v = _check(q, k, v)
+    q, k, v = _check(q, k, v, causal)
+    if q.shape != k.shape:
+        raise ValueError("the backward takes as many queries as keys")
     o = np.asarray(o, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     B, H, N, d = q.shape
@@ -156,11 +164,12 @@ def online_forward(q, k, v, scale, causal, block, descending=False):
     When every score seen so far is masked (m' = -inf) the subtraction base is
     taken as 0 so that e^(-inf - (-inf)) never forms a NaN.
     """
-    q, k, v = _check(q, k, v)
+    q, k, v = _check(q, k, v, causal)
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     o = np.empty_like(q)
     lse = np.empty((B, H, N), dtype=np.float64)
-    starts = list(range(0, N, block))
+    starts = list(range(0, Nk, block))
     if descending:
         starts.reverse()
     rows = np.arange(N)
@@ -170,7 +179,7 @@ def online_forward(q, k, v, scale, causal, block, descending=False):
             l = np.zeros(N)
             acc = np.zeros((N, d))
             for t0 in starts:
-                cols = np.arange(t0, min(N, t0 + block))
+                cols = np.arange(t0, min(Nk, t0 + block))
                 s = scale * (q[b, h] @ k[b, h, cols].T)
                 if causal:
                     s[rows[:, None] < cols[None, :]] = -np.inf
