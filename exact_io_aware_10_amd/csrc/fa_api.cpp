@@ -19,7 +19,7 @@ int check_common(int B, int H, int N, int d, float scale, int causal, bool* empt
   *empty = false;
   if (B < 0 || H < 0 || N < 0) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
-  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (d != kHeadDim) return FA_ERR_UNSUPPORTED;
   if (B == 0 || H == 0 || N == 0) {
     *empty = true;
@@ -185,7 +185,7 @@ int fa_fwd_fp8(const void* q8, const int* qexp, const void* k8, const int* kexp,
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "success";
-    case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size, bad scale or causal flag)";
+    case FA_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size, non-finite scale or bad causal flag)";
     case FA_ERR_UNSUPPORTED: return "unsupported (head dim other than 128, misaligned pointer, or size overflow)";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than fa_bwd_workspace_size()";
     case FA_ERR_HIP: return "HIP runtime rejected the launch";

@@ -133,7 +133,8 @@ __global__ __launch_bounds__(KV_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
 void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
                      const float* __restrict__ ws, uint16_t* __restrict__ dk,
-                     uint16_t* __restrict__ dv, int BH, int N, float sl2, float scale) {
+                     uint16_t* __restrict__ dv, int BH, int N, float sl2, float scale,
+                     uint32_t kkeep, uint32_t kflip) {
   __shared__ __attribute__((aligned(16))) char smem[KV_SMEM];
   const uint32_t smem_lds = lds_addr(smem);  // LDS byte address of smem (wave-uniform)
 
@@ -170,14 +171,17 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     dma16(rv, smem_lds + KV_V_OFF + row0 * kRowBytes,
           (uint32_t)(k0 + row) * kRowBytes + ((ld_pc ^ swz(row)) << 4));
   }
-  // K as the B operand of S = Q K^T: lane holds K[kw + 32 g + col][16 kc + 8 h .. + 7].
+  // K as the B operand of S = Q K^T: lane holds K[kw + 32 g + col][16 kc + 8 h .. + 7],
+  // negated for a negative scale and cleared for scale 0 (sl2 is |scale| log2 e;
+  // dK = scale dS^T Q takes the signed scale at the store).
   bf16x8 kf[2][8];
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc)
       kf[g][kc] = __builtin_bit_cast(
-          bf16x8, buf_load16(rk, (uint32_t)(kw + 32 * g + col) * kRowBytes + (2 * kc + h) * 16));
+          bf16x8, signed_operand(buf_load16(rk, (uint32_t)(kw + 32 * g + col) * kRowBytes + (2 * kc + h) * 16),
+                                 kkeep, kflip));
   // Touch kf once here: the compiler waits for the loads at this point, and
   // knows from then on that they have arrived.
 #pragma unroll
@@ -514,7 +518,7 @@ __global__ __launch_bounds__(DQ_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1
 void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
                    const float* __restrict__ ws, uint16_t* __restrict__ dq, int BH, int N, int nqb,
-                   float sl2, float scale) {
+                   float sl2, float scale, uint32_t qkeep, uint32_t qflip) {
   __shared__ __attribute__((aligned(16))) char smem[DQ_SMEM];
   const uint32_t smem_lds = lds_addr(smem);
 
@@ -540,16 +544,27 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const rsrc_t rD = make_rsrc(ws + (size_t)bh * N, (uint32_t)N * 4);
   const rsrc_t rL = make_rsrc(ws + rows + (size_t)bh * N, (uint32_t)N * 4);
 
-  // Q^T and dO^T as B operands (zero past N), Q straight into AGPRs: lane
-  // holds Q[q0w + 32 g + col][16 kc + 8 h .. + 7].  Waited for below.
+  // Q^T and dO^T as B operands (zero past N): lane holds
+  // Q[q0w + 32 g + col][16 kc + 8 h .. + 7].  Q is negated for a negative
+  // scale and cleared for scale 0 (sl2 is |scale| log2 e; dQ = scale dS K
+  // takes the signed scale at the store), then moved to AGPRs.  dO is waited
+  // for below.
   bf16x8 qf[2][8], df[2][8];
+  u32x4 qraw[2][8];
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       const uint32_t off = (uint32_t)(q0w + 32 * g + col) * kRowBytes + (2 * kc + h) * 16;
-      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=a"(qf[g][kc]) : "v"(off), "s"(rq) : "memory");
+      qraw[g][kc] = buf_load16(rq, off);
       asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(df[g][kc]) : "v"(off), "s"(rdo) : "memory");
+    }
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const bf16x8 qv = __builtin_bit_cast(bf16x8, signed_operand(qraw[g][kc], qkeep, qflip));
+      asm volatile("" : "=a"(qf[g][kc]) : "0"(qv));
     }
   float l2[2], dd[2];
 #pragma unroll
@@ -800,14 +815,15 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
                            const float* ws, void* dk, void* dv, int B, int H, int N, float scale,
                            int causal, hipStream_t stream) {
   const int BH = B * H;
-  const float sl2 = scale * kLog2e;
+  const signed_scale sc = split_scale(scale, kSignBitsBf16);
+  const float sl2 = sc.mag * kLog2e;
   const int nkb = (N + KV_BK - 1) / KV_BK;
   dim3 grid((unsigned)(nkb * BH)), block(KV_THREADS);
   auto kern = causal ? bwd_dkdv_kernel<true> : bwd_dkdv_kernel<false>;
   hipLaunchKernelGGL(kern, grid, block, 0, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                      static_cast<const uint16_t*>(dO), ws, static_cast<uint16_t*>(dk),
-                     static_cast<uint16_t*>(dv), BH, N, sl2, scale);
+                     static_cast<uint16_t*>(dv), BH, N, sl2, scale, sc.keep, sc.flip);
   return hipGetLastError();
 }
 
@@ -815,14 +831,15 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          const float* ws, void* dq, int B, int H, int N, float scale, int causal,
                          hipStream_t stream) {
   const int BH = B * H;
-  const float sl2 = scale * kLog2e;
+  const signed_scale sc = split_scale(scale, kSignBitsBf16);
+  const float sl2 = sc.mag * kLog2e;
   const int nqb = (N + DQ_BQ - 1) / DQ_BQ;
   dim3 grid((unsigned)(nqb * BH)), block(DQ_THREADS);
   auto kern = causal ? bwd_dq_kernel<true> : bwd_dq_kernel<false>;
   hipLaunchKernelGGL(kern, grid, block, 0, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                      static_cast<const uint16_t*>(dO), ws, static_cast<uint16_t*>(dq), BH, N, nqb,
-                     sl2, scale);
+                     sl2, scale, sc.keep, sc.flip);
   return hipGetLastError();
 }
 

@@ -99,6 +99,22 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// A register-held operand under a signed softmax scale: every element's bits
+// ANDed with `keep` and XORed with `flip` (negated for a negative scale,
+// cleared for scale 0; the host side derives the two words).
+__device__ __forceinline__ u32x4 signed_operand(u32x4 u, uint32_t keep, uint32_t flip) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] = (u[i] & keep) ^ flip;
+  return u;
+}
+
+// acc + the two bf16 values packed in `pair`, in fp32 (one v_dot2c_f32_bf16
+// against (1, 1): the products are exact).
+__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+}
+
 __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5,
                                         float a6, float a7) {
   u32x4 u = {pack_bf16(a0, a1), pack_bf16(a2, a3), pack_bf16(a4, a5), pack_bf16(a6, a7)};

@@ -1,10 +1,9 @@
 // FP8 forward with incoherent processing: Q, K and V rotated by a random
 // Hadamard transform over the head dimension, quantised per block of 64 rows
-// to OCP E4M3 with power-of-two scales, and attended with gfx950's FP8 MFMA
-// ("Interrogating the GPU, part 5: FlashAttention", section "What did
-// FlashAttention-3 do with Hopper?": keys and values quantised per block
-// after a random Hadamard rotation; "FlashAttention versions", section
-// "FlashAttention-3": block quantisation with incoherent processing).
+// to OCP E4M3 with power-of-two scales, and attended with gfx950's FP8 MFMA:
+// the FP8 scheme of "Interrogating the GPU, part 5: FlashAttention", section
+// "What did FlashAttention-3 do with Hopper?", and of "FlashAttention
+// versions", section "FlashAttention-3", built for this GPU.
 //
 // With sigma a random sign vector and H the 128 x 128 Sylvester Hadamard
 // matrix (entries +-1, H H = 128 I):
@@ -174,7 +173,8 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const int* __restrict__ qexp
                     const uint8_t* __restrict__ k8, const int* __restrict__ kexp,
                     const uint8_t* __restrict__ v8, const int* __restrict__ vexp,
                     const float* __restrict__ signs, uint16_t* __restrict__ o,
-                    float* __restrict__ lse, int BH, int N, int nqb, float sl2base) {
+                    float* __restrict__ lse, int BH, int N, int nqb, float sl2base,
+                    uint32_t qkeep, uint32_t qflip) {
   __shared__ __attribute__((aligned(16))) char k_lds0[F8_TILE];
   __shared__ __attribute__((aligned(16))) char k_lds1[F8_TILE];
   __shared__ __attribute__((aligned(16))) char v_lds0[F8_TILE];
@@ -205,7 +205,8 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const int* __restrict__ qexp
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const uint32_t off = (uint32_t)qrow * F8_ROWB + 64 * kk + 32 * h;
-    qf[kk] = join8(buf_load16(rq, off), buf_load16(rq, off + 16));
+    qf[kk] = join8(signed_operand(buf_load16(rq, off), qkeep, qflip),
+                   signed_operand(buf_load16(rq, off + 16), qkeep, qflip));
   }
   const int qe = qexp[(size_t)bh * nkt + min(q0w / F8_BLK, nkt - 1)];
   const float sl2q = ldexpf(sl2base, qe);
@@ -429,12 +430,15 @@ hipError_t launch_fwd_fp8(const void* q8, const int* qexp, const void* k8, const
                           int B, int H, int N, float scale, int causal, hipStream_t stream) {
   const int BH = B * H;
   const int nqb = (N + F8_BR - 1) / F8_BR;
-  const float sl2base = scale * kLog2e / (float)kD;  // Q' K'^T = 128 Q K^T
+  // |scale|; the sign (or a zero scale) is folded into the Q codes, whose
+  // sign bits are flipped (or cleared) as they are loaded.
+  const signed_scale sc = split_scale(scale, kSignBitsFp8);
+  const float sl2base = sc.mag * kLog2e / (float)kD;  // Q' K'^T = 128 Q K^T
   dim3 grid((unsigned)(nqb * BH)), block(F8_THREADS);
   auto kern = causal ? fwd_fp8_kernel<true> : fwd_fp8_kernel<false>;
   hipLaunchKernelGGL(kern, grid, block, 0, stream, static_cast<const uint8_t*>(q8), qexp,
                      static_cast<const uint8_t*>(k8), kexp, static_cast<const uint8_t*>(v8), vexp,
-                     signs, static_cast<uint16_t*>(o), lse, BH, N, nqb, sl2base);
+                     signs, static_cast<uint16_t*>(o), lse, BH, N, nqb, sl2base, sc.keep, sc.flip);
   return hipGetLastError();
 }
 

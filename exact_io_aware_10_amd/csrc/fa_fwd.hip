@@ -50,7 +50,8 @@ template <bool CAUSAL>
 __global__ __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-                float* __restrict__ lse, int BH, int N, int nqb, float sl2) {
+                float* __restrict__ lse, int BH, int N, int nqb, float sl2, uint32_t qkeep,
+                uint32_t qflip) {
   // [buffer][K | V] tiles, each 64 rows x 256 bytes, swizzled (tile_off).
   __shared__ __attribute__((aligned(16))) char k_lds0[FWD_TILE];
   __shared__ __attribute__((aligned(16))) char k_lds1[FWD_TILE];
@@ -76,11 +77,13 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const rsrc_t rk = make_rsrc(k + head, head_bytes);
   const rsrc_t rv = make_rsrc(v + head, head_bytes);
 
-  // Q^T as the B operand: lane holds Q[qrow][16 kc + 8 h .. + 7] (zero past N).
+  // Q^T as the B operand: lane holds Q[qrow][16 kc + 8 h .. + 7] (zero past N),
+  // negated for a negative scale and cleared for scale 0 (sl2 is |scale| log2 e).
   bf16x8 qf[8];
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc)
-    qf[kc] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)qrow * kRowBytes + (2 * kc + h) * 16));
+    qf[kc] = __builtin_bit_cast(
+        bf16x8, signed_operand(buf_load16(rq, (uint32_t)qrow * kRowBytes + (2 * kc + h) * 16), qkeep, qflip));
 
   const int kend = CAUSAL ? min(N, q0 + FWD_BR) : N;
   const int ntiles = (kend + FWD_BC - 1) / FWD_BC;
@@ -134,7 +137,13 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
   float m = -INFINITY;  // reference maximum, log2 domain of the scaled scores
-  float l = 0.f;        // running sum over this lane's half of each tile
+  float l = 0.f;        // running sum of P over this lane's half of each tile (for LSE)
+  float lr = 0.f;       // the same sum of P as rounded to bf16 for the P V product
+  // O is divided by lr: normalised by exactly the weights it was built from,
+  // O stays a convex combination of V rows, and on rows dominated by one key
+  // (large score ranges, where the stale reference maximum leaves that key's
+  // P anywhere in [1, 2^kTau] and its bf16 rounding would otherwise move O by
+  // up to 2^-9 |V|) the rounding cancels.  LSE keeps the fp32 sum l.
 
   auto step = [&](int t, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
@@ -188,6 +197,7 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m - mnew);
         m = mnew;
         l *= alpha;
+        lr *= alpha;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -214,6 +224,9 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           const int b = 8 * u;
           pb[st][u] = pack8(s[st][b], s[st][b + 1], s[st][b + 2], s[st][b + 3], s[st][b + 4],
                             s[st][b + 5], s[st][b + 6], s[st][b + 7]);
+          const u32x4 pw = __builtin_bit_cast(u32x4, pb[st][u]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lr = add_bf16_pair(pw[e], lr);
         }
 
 #pragma unroll
@@ -241,8 +254,9 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 
   const float lt = halves_sum(l);
+  const float lrt = halves_sum(lr);
   if (qrow < N) {
-    const float inv = 1.f / lt;
+    const float inv = 1.f / lrt;
     char* orow = reinterpret_cast<char*>(o + head) + (size_t)qrow * kRowBytes;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -269,7 +283,9 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // loop) and keeps its own online-softmax state (m_w, l_w, O_w).  At the end
 // the four partial states merge by the rescale rule of the online softmax:
 //   M = max_w m_w,  L = sum_w 2^(m_w - M) l_w,
-//   O = sum_w 2^(m_w - M) O_w / L,  LSE = ln2 (M + log2 L),
+//   O = sum_w 2^(m_w - M) O_w / L',  LSE = ln2 (M + log2 L),
+// where L' merges the same way the sums of P as rounded to bf16 for the P V
+// products (so that O is normalised by exactly the weights it was built from),
 // through LDS, each wave producing 32 of the 128 output dimensions.
 constexpr int SPL_QW = 32;                         // query rows per workgroup
 constexpr int SPL_WAVES = 4;
@@ -279,14 +295,15 @@ constexpr int SPL_WAVE_LDS = 4 * SPL_TILE;         // [buffer][K | V] per wave
 constexpr int SPL_SMEM = SPL_WAVES * SPL_WAVE_LDS;  // 128 KiB
 constexpr int SPL_LOADS = SPL_TILE / 1024;         // 1 KiB LDS-direct loads per tile and tensor
 constexpr int SPL_PART = 64 * 16;                  // floats in one O^T block (64 lanes x 16)
-static_assert((SPL_WAVES * SPL_WAVES * SPL_PART + 2 * SPL_WAVES * SPL_QW) * 4 <= SPL_SMEM,
+static_assert((SPL_WAVES * SPL_WAVES * SPL_PART + 3 * SPL_WAVES * SPL_QW) * 4 <= SPL_SMEM,
               "the merge buffers must fit the tile buffers they reuse");
 
 template <bool CAUSAL>
 __global__ __launch_bounds__(SPL_WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                       const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-                      float* __restrict__ lse, int BH, int N, int nqb, float sl2) {
+                      float* __restrict__ lse, int BH, int N, int nqb, float sl2, uint32_t qkeep,
+                      uint32_t qflip) {
   __shared__ __attribute__((aligned(16))) char smem[SPL_SMEM];
 
   const int tid = threadIdx.x;
@@ -309,7 +326,8 @@ void fwd_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   bf16x8 qf[8];
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc)
-    qf[kc] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)qrow * kRowBytes + (2 * kc + h) * 16));
+    qf[kc] = __builtin_bit_cast(
+        bf16x8, signed_operand(buf_load16(rq, (uint32_t)qrow * kRowBytes + (2 * kc + h) * 16), qkeep, qflip));
 
   const int kend = CAUSAL ? min(N, q0 + SPL_QW) : N;
   const int ntiles = (kend + SPL_BC - 1) / SPL_BC;
@@ -359,7 +377,12 @@ void fwd_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
   float m = -INFINITY;
-  float l = 0.f;
+  float l = 0.f;   // row sum of P in fp32: the LSE's
+  float lr = 0.f;  // row sum of P as rounded to bf16 for the P V product: O's divisor
+  // Dividing O by the sum of the same rounded weights that the P V product
+  // used keeps O a convex combination of V rows: on rows dominated by one or
+  // two keys (large score ranges) the rounding of the dominant P then cancels
+  // instead of moving O by up to 2^-9 |V|.
 
   if (nmine > 0) issue(0, 0);
   for (int j = 0; j < nmine; ++j) {
@@ -401,6 +424,7 @@ void fwd_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m - mnew);
       m = mnew;
       l *= alpha;
+      lr *= alpha;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -420,6 +444,9 @@ void fwd_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     for (int u = 0; u < 2; ++u) {
       const bf16x8 pb = pack8(s[8 * u], s[8 * u + 1], s[8 * u + 2], s[8 * u + 3], s[8 * u + 4],
                               s[8 * u + 5], s[8 * u + 6], s[8 * u + 7]);
+      const u32x4 pw = __builtin_bit_cast(u32x4, pb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lr = add_bf16_pair(pw[e], lr);
       const char* rb = vb + 16 * u * kRowBytes;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
@@ -431,6 +458,7 @@ void fwd_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   // are reused: part[w][mb] holds wave w's O^T block mb (element group g of
   // lane x at float4 index 64 g + x), stats[w] its m and row sum per query.
   const float lt = halves_sum(l);
+  const float lrt = halves_sum(lr);
   __syncthreads();
   float* part = reinterpret_cast<float*>(smem);
   float* stats = part + SPL_WAVES * SPL_WAVES * SPL_PART;
@@ -442,24 +470,26 @@ void fwd_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       *reinterpret_cast<f32x4*>(part + (wave * SPL_WAVES + mb) * SPL_PART + 4 * (64 * g + lane)) = w4;
     }
   if (h == 0) {
-    stats[(2 * wave) * SPL_QW + col] = m;
-    stats[(2 * wave + 1) * SPL_QW + col] = lt;
+    stats[(3 * wave) * SPL_QW + col] = m;
+    stats[(3 * wave + 1) * SPL_QW + col] = lt;
+    stats[(3 * wave + 2) * SPL_QW + col] = lrt;
   }
   __syncthreads();
 
   float mw[SPL_WAVES], M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < SPL_WAVES; ++w) {
-    mw[w] = stats[(2 * w) * SPL_QW + col];
+    mw[w] = stats[(3 * w) * SPL_QW + col];
     M = fmaxf(M, mw[w]);
   }
-  float L = 0.f, cw[SPL_WAVES];
+  float L = 0.f, Lr = 0.f, cw[SPL_WAVES];
 #pragma unroll
   for (int w = 0; w < SPL_WAVES; ++w) {
     cw[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - M);  // a wave without keys adds nothing
-    L += cw[w] * stats[(2 * w + 1) * SPL_QW + col];
+    L += cw[w] * stats[(3 * w + 1) * SPL_QW + col];
+    Lr += cw[w] * stats[(3 * w + 2) * SPL_QW + col];
   }
-  const float inv = 1.f / L;
+  const float inv = 1.f / Lr;
   // This wave writes output dimensions 32 wave .. 32 wave + 31 (block mb = wave).
   f32x16 ob;
 #pragma unroll
@@ -496,16 +526,17 @@ hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o
                             int B, int H, int N, float scale, int causal, hipStream_t stream) {
   const int BH = B * H;
   const int nqb = (N + SPL_QW - 1) / SPL_QW;
-  const float sl2 = scale * kLog2e;
+  const signed_scale sc = split_scale(scale, kSignBitsBf16);
+  const float sl2 = sc.mag * kLog2e;
   dim3 grid((unsigned)(nqb * BH)), block(SPL_WAVES * 64);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   uint16_t* oo = static_cast<uint16_t*>(o);
   if (causal)
-    hipLaunchKernelGGL(fwd_split_kernel<true>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2);
+    hipLaunchKernelGGL(fwd_split_kernel<true>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2, sc.keep, sc.flip);
   else
-    hipLaunchKernelGGL(fwd_split_kernel<false>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2);
+    hipLaunchKernelGGL(fwd_split_kernel<false>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2, sc.keep, sc.flip);
   return hipGetLastError();
 }
 
@@ -513,16 +544,17 @@ hipError_t launch_fwd_rows(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int N, float scale, int causal, hipStream_t stream) {
   const int BH = B * H;
   const int nqb = (N + FWD_BR - 1) / FWD_BR;
-  const float sl2 = scale * kLog2e;
+  const signed_scale sc = split_scale(scale, kSignBitsBf16);
+  const float sl2 = sc.mag * kLog2e;
   dim3 grid((unsigned)(nqb * BH)), block(FWD_THREADS);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   uint16_t* oo = static_cast<uint16_t*>(o);
   if (causal)
-    hipLaunchKernelGGL(fwd_kernel<true>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2);
+    hipLaunchKernelGGL(fwd_kernel<true>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2, sc.keep, sc.flip);
   else
-    hipLaunchKernelGGL(fwd_kernel<false>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2);
+    hipLaunchKernelGGL(fwd_kernel<false>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2, sc.keep, sc.flip);
   return hipGetLastError();
 }
 

@@ -4,8 +4,31 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa {
+
+// A signed softmax scale, as the kernels take it.  The scores are
+// scale * q . k; the kernels work with the magnitude `mag` (> 0) and fold the
+// sign into the operand they hold in registers (Q, or K in the dK/dV kernel):
+// its bit patterns are ANDed with `keep` and XORed with `flip`.  Negating
+// every element is exact, and so the scores come out exactly negated; for
+// scale = 0 the operand is cleared, every visible score is exactly 0 and the
+// weights are uniform over the visible keys (mag is then an arbitrary
+// positive value that multiplies zeros).  `sign_bits` holds the sign bit of
+// every element packed in a 32-bit word (0x80008000 for bf16 pairs,
+// 0x80808080 for four FP8 codes).
+struct signed_scale {
+  float mag;
+  uint32_t keep, flip;
+};
+inline signed_scale split_scale(float scale, uint32_t sign_bits) {
+  if (scale > 0.f) return {scale, 0xffffffffu, 0u};
+  if (scale < 0.f) return {-scale, 0xffffffffu, sign_bits};
+  return {1.f, 0u, 0u};
+}
+constexpr uint32_t kSignBitsBf16 = 0x80008000u;
+constexpr uint32_t kSignBitsFp8 = 0x80808080u;
 
 // launch_fwd picks the row-block kernel (launch_fwd_rows) or, for grids too
 // small to fill the chip, the key-split kernel (launch_fwd_split).

@@ -22,7 +22,10 @@
  *     when any of B,
  *     H, N is 0 there is nothing to compute and the call returns FA_OK
  *     without touching any pointer.
- *   - scale must be finite and > 0 (the scores are scale * q . k).
+ *   - scale must be finite; any sign, and zero, is accepted (the scores are
+ *     scale * q . k; scale = 0 gives uniform weights over the visible keys).
+ *     The scaled scores are formed in float32, so |scale * q . k| must stay
+ *     below 2^127 for the results to be finite.
  *   - causal: 0 = every key visible; 1 = key j visible to query i iff j <= i.
  *   - Inputs are read only.  Outputs are fully overwritten, never accumulated
  *     into.  No output may alias an input or another output (not detected).
@@ -44,7 +47,7 @@ extern "C" {
 
 typedef enum {
   FA_OK = 0,
-  FA_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, bad scale/causal */
+  FA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, non-finite scale, bad causal */
   FA_ERR_UNSUPPORTED = 2,  /* d != 128, misaligned pointer, size overflow */
   FA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
   FA_ERR_HIP = 4           /* the HIP runtime rejected a launch */

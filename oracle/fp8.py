@@ -8,14 +8,31 @@ the OCP FP8 E4M3 format.
 
 Sources:
   [P1] "Interrogating the GPU, part 5: FlashAttention", section "What did
-       FlashAttention-3 do with Hopper?": keys and values are quantised per
-       block after a random Hadamard rotation, which spreads outliers across
-       the block (2.6 times lower error than plain FP8).
-  [P2] "FlashAttention versions", section "FlashAttention-3": block-level
-       quantisation with incoherent processing, as opposed to per-tensor
-       quantisation that degrades on outliers.
+       FlashAttention-3 do with Hopper?": FP8 keys and values with one scale
+       per block, preceded by a random orthogonal (Hadamard) mixing of the
+       head dimension so that a few large features no longer set a whole
+       block's scale; the page reports the error of that scheme against
+       plain FP8 (a factor 2.6).
+  [P2] "FlashAttention versions", section "FlashAttention-3": per-block
+       scales with this "incoherent processing", contrasted with one scale
+       per tensor.
   [P1] section "How can you softmax a row you never see whole?" and the
        FlashAttention-4 section (conditional rescale) for the online softmax.
+
+Two functions compute the FP8 forward:
+  * forward_reference follows only the pages and the readings below that the
+    pages force (rotation, per-block E4M3, P in E4M3): no tiles, no stale
+    maxima, P taken against each row's true maximum.  Tests compare the GPU's
+    error against exact attention with this function's error, and check the
+    pages' claim (the rotation lowers the error on outlier features) on GPU
+    output against it.
+  * forward_emulated additionally makes the choices of one tiled schedule
+    (TILE keys per step, the conditional rescale with threshold TAU decided
+    for WAVE_ROWS query rows at once, P scaled by 2^(8 - TAU) before its
+    rounding), so that its E4M3 roundings of P fall where a kernel with that
+    schedule rounds them; it is the tight parity check of such a kernel.
+    These choices are readings of this oracle, not of the pages (which fix
+    no tile size, threshold or scaling of P).
 
 Readings adopted where the pages are silent:
   * the rotation is R = diag(sigma) H over the head dimension d = 128, with H
@@ -42,7 +59,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["e4m3_decode", "e4m3_encode", "fwht32", "rotate", "block_exponent",
-           "quantize_rows", "quantize_tensor", "forward_emulated", "TAU", "TILE", "QBLOCK"]
+           "quantize_rows", "quantize_tensor", "forward_emulated", "forward_reference",
+           "TAU", "TILE", "QBLOCK"]
 
 TAU = 2.0        # conditional-rescale threshold (log2 units) of the FP8 path
 TILE = 64        # keys per tile (and rows per quantisation block)
@@ -231,3 +249,57 @@ def forward_emulated(q, k, v, signs, scale, causal, quantize=True, rotate_first=
                 o[b, h] = op
             lse[b, h] = (m + np.log2(l)) * np.log(2.0)
     return o, lse
+
+
+def forward_reference(q, k, v, signs, scale, causal, rotate_first=True, quantize=True,
+                      row_block=1024):
+    """FP8 attention as the pages describe it, with no schedule: rotate Q, K
+    and V (unless rotate_first is False: plain per-block FP8), quantise each
+    64-row block to E4M3, form every score of a row from the dequantised
+    codes, take the softmax against the row's true maximum, round P times 2^8
+    (so that the largest weight, 1, lands on the E4M3 value 256) to E4M3 for
+    the P V' product, divide by the row sum of the unrounded weights, undo
+    the rotation, and round O to bf16 as the GPU path stores it.
+
+    quantize=False skips every E4M3 rounding and the bf16 rounding of O: the
+    result is then exact attention.  Returns (O, LSE), LSE the natural
+    log-sum-exp of the scores it forms."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, N, d = q.shape
+    sg = np.asarray(signs, dtype=np.float64)
+    hm = fwht32(np.eye(d, dtype=np.float32)).astype(np.float64)  # Sylvester H, H H = d I
+    if quantize:
+        qr, kr, vr = (_dequant(*quantize_tensor(x, signs, rotate_first)) for x in (q, k, v))
+    elif rotate_first:
+        qr, kr, vr = ((x * sg) @ hm for x in (q, k, v))
+    else:
+        qr, kr, vr = q, k, v
+    # with the rotation, q'.k' = d q.k; the score multiplier takes the d out
+    mult = scale / d if rotate_first else scale
+    o = np.empty((B, H, N, d))
+    lse = np.empty((B, H, N))
+    keys = np.arange(N)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, N, row_block):
+                rows = np.arange(r0, min(N, r0 + row_block))
+                s = mult * (qr[b, h, rows] @ kr[b, h].T)
+                if causal:
+                    s[rows[:, None] < keys[None, :]] = -np.inf
+                m = s.max(axis=1)
+                w = np.exp(s - m[:, None])
+                denom = w.sum(axis=1)
+                wq = e4m3_decode(e4m3_encode(w * 256.0)) * (1.0 / 256.0) if quantize else w
+                out = (wq @ vr[b, h]) / denom[:, None]
+                if rotate_first:
+                    out = sg * (out @ hm) * (1.0 / d)  # (x H / d) o sigma undoes the rotation
+                o[b, h, rows] = out
+                lse[b, h, rows] = m + np.log(denom)
+    if not quantize:
+        return o, lse
+    # round to bf16, nearest even, as the output is stored
+    u = o.astype(np.float32).view(np.uint32).astype(np.uint64)
+    r = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32)
+    return r.view(np.float32).astype(np.float64), lse

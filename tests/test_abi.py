@@ -60,8 +60,13 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
     ((1, 1, 16, 64, 0.1, 0, 0), 2),
     ((1, 1, 16, 128, float("nan"), 0, 0), 1),
     ((1, 1, 16, 128, float("inf"), 0, 0), 1),
-    ((1, 1, 16, 128, 0.0, 0, 0), 1),
-    ((1, 1, 16, 128, -0.5, 0, 0), 1),
+    ((1, 1, 16, 128, float("-inf"), 0, 0), 1),
+    # Any finite scale passes validation (shown on empty problems, which
+    # return before touching a pointer); the kernels' results at scale 0 and
+    # below are checked by the GPU tests.
+    ((1, 1, 0, 128, 0.0, 0, 0), 0),
+    ((1, 1, 0, 128, -0.5, 1, 0), 0),
+    ((1, 1, 0, 128, -3e38, 0, 0), 0),
     ((1, 1, 16, 128, 0.1, 2, 0), 1),
     ((-1, 1, 16, 128, 0.1, 0, 0), 1),
     ((1, -1, 16, 128, 0.1, 0, 0), 1),

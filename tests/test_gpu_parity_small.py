@@ -83,10 +83,11 @@ def _scaled_bar(ref):
 
 
 # The softmax scale is a runtime argument: a near-zero scale (almost uniform
-# attention) and a scale 5.7 times the usual one (scores of standard
-# deviation 5.7, sharply peaked rows), forward through both kernels and
-# backward.
-@pytest.mark.parametrize("scale", [1e-4, 0.5])
+# attention), a scale 5.7 times the usual one (scores of standard deviation
+# 5.7, sharply peaked rows), exactly zero (uniform weights over the visible
+# keys; dQ = dK = 0) and negative scales (the kernels fold the sign into the
+# operand they hold in registers), forward through both kernels and backward.
+@pytest.mark.parametrize("scale", [1e-4, 0.5, 0.0, -fa_inputs.SCALE, -0.5])
 @pytest.mark.parametrize("causal", [False, True])
 def test_other_scales(fa, scale, causal):
     import torch

@@ -34,6 +34,19 @@ MUTANTS = [
     ("rescale of l forgotten", "l[g] *= alpha\n", "l[g] *= 1.0\n"),
     ("dequantisation exponent sign", "return e4m3_decode(codes) * np.exp2(rows_e)[..., None]",
      "return e4m3_decode(codes) * np.exp2(-rows_e)[..., None]"),
+    ("reference: score gain of the rotation dropped", "mult = scale / d if rotate_first else scale",
+     "mult = scale"),
+    ("reference: P scale not undone", "e4m3_encode(w * 256.0)) * (1.0 / 256.0)",
+     "e4m3_encode(w * 256.0))"),
+    ("reference: un-rotation without 1/d", "out = sg * (out @ hm) * (1.0 / d)", "out = sg * (out @ hm)"),
+    ("reference: un-rotation without signs", "out = sg * (out @ hm) * (1.0 / d)",
+     "out = (out @ hm) * (1.0 / d)"),
+    ("reference: normalised by the rounded weights' count", "out = (wq @ vr[b, h]) / denom[:, None]",
+     "out = (wq @ vr[b, h]) / w.shape[1]"),
+    ("reference: P against the row sum instead of the maximum", "w = np.exp(s - m[:, None])",
+     "w = np.exp(s - np.log(np.exp(s).sum(axis=1))[:, None])"),
+    ("reference: output rounded toward zero", "r = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16)",
+     "r = ((u >> 16) << 16)"),
 ]
 
 
@@ -94,6 +107,35 @@ def _pins(mod):
         o, lse = mod.forward_emulated(q, k, v, s, fa_inputs.SCALE, True)
         return np.abs(o - o_ref).max() <= 0.15 and np.abs(lse - lse_ref).max() <= 0.15
     check("error budget", budget)
+
+    def ref_exact():
+        o, lse = mod.forward_reference(q3, k3, v3, s, fa_inputs.SCALE, True, quantize=False)
+        return np.abs(o - o3_ref).max() <= 1e-11 and np.abs(lse - lse3_ref).max() <= 1e-11
+    check("reference exact without rounding", ref_exact)
+
+    def ref_budget():
+        o, lse = mod.forward_reference(q, k, v, s, fa_inputs.SCALE, True)
+        return np.abs(o - o_ref).max() <= 0.15 and np.abs(lse - lse_ref).max() <= 0.15
+    check("reference error budget", ref_budget)
+
+    def ref_bf16():
+        o, _ = mod.forward_reference(q, k, v, s, fa_inputs.SCALE, True)
+        f = o.astype(np.float32)
+        nearest = np.abs(o - o_ref) <= 2.0 ** -8 * np.abs(o_ref) + 0.15
+        return np.all((f.view(np.uint32) & 0xFFFF) == 0) and np.all(nearest)
+    check("reference bf16 output", ref_bf16)
+
+    def ref_rne():
+        # Uniform weights (scale 0) over two V rows a e_0 and b e_0 with a = 1
+        # and b = 1.5 2^-8, both exact in one E4M3 block (exponent -8): every
+        # step is exact in fp64 and O_00 = (a + b) / 2 = 0.5 (1 + 2^-8 + 2^-9),
+        # which bf16 (ulp 2^-8 there) rounds to nearest as 0.5 (1 + 2^-7).
+        qq = np.zeros((1, 1, 2, 128))
+        vv = np.zeros((1, 1, 2, 128))
+        vv[0, 0, 0, 0], vv[0, 0, 1, 0] = 1.0, 1.5 * 2.0 ** -8
+        o, _ = mod.forward_reference(qq, qq, vv, s, 0.0, False)
+        return o[0, 0, 0, 0] == 0.5 * (1 + 2.0 ** -7) and np.all(o[0, 0, :, 1:] == 0)
+    check("reference rounding", ref_rne)
 
     def quant():
         codes, exps = mod.quantize_tensor(v, s)
