@@ -16,12 +16,30 @@ around every kernel of every timed step.
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
-import platform
+import statistics
 import sys
 import time
+
+
+def _oracle_threads() -> int:
+    """BLAS threads for the oracle timing: the cores this process may run on
+    (its affinity mask), capped by OMP_NUM_THREADS where the host sets one
+    (the CPU share a shared host grants this process)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return n
+
+
+# Set before numpy is first imported (the BLAS library reads these once, at load).
+ORACLE_THREADS = _oracle_threads()
+for _var in ("OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+    os.environ[_var] = str(ORACLE_THREADS)
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -59,19 +77,40 @@ def traffic_for(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(x, w, heads: int):
-    """The fp64 oracle (forward + backward) on the first `heads` heads."""
-    import numpy as np
-    from oracle import attention as ora
+# Oracle sample per workload: (batch 0) heads 0 .. n-1, sized for about
+# 10-30 s of CPU work on 16 cores.
+CPU_SAMPLE_HEADS = {"fwd_b1_h1_n512": 1, "fwd_b4_h32_n2048": 32, "causal_b1_h64_n8192": 16,
+                    "causal_b2_h16_n4096": 8, "causal_b1_h8_n32768_std4": 1}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (the field lscpu reports as "Model name")."""
     try:
-        from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()
-                     if p.get("user_api") == "blas"), default=1)
-    except Exception:  # pragma: no cover
-        cores = 1
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x, w, heads: int):
+    """The fp64 oracle (forward, and backward where the workload has one) on
+    heads 0 .. heads-1 of batch 0, after an untimed warm-up on a small head."""
+    from oracle import attention as ora
+    from threadpoolctl import threadpool_info
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    has_bwd = "do" in x
+    # Warm-up: the same calls on the first 256 rows of head 0 (loads the BLAS
+    # library, starts its threads, faults in the code paths).
+    wq = fa_inputs.make(1, 1, 256, seed=w["seed"], qk_std=w["qk_std"], with_do=True)
+    WQ, WK, WV, WD = (fa_inputs.bf16_bits_to_f64(wq[n]) for n in ("q", "k", "v", "do"))
+    wo, _ = ora.forward(WQ, WK, WV, fa_inputs.SCALE, w["causal"])
+    if has_bwd:
+        ora.backward(WQ, WK, WV, wo, WD, fa_inputs.SCALE, w["causal"])
     sl = (slice(0, 1), slice(0, heads))
     Q, K, V = (fa_inputs.bf16_bits_to_f64(x[n][sl]) for n in "qkv")
-    has_bwd = "do" in x
     t0 = time.perf_counter()
     o, _ = ora.forward(Q, K, V, fa_inputs.SCALE, w["causal"])
     flops = acc.fwd_flops(1, heads, w["N"], 128, w["causal"])
@@ -80,17 +119,46 @@ def cpu_baseline(x, w, heads: int):
         ora.backward(Q, K, V, o, DO, fa_inputs.SCALE, w["causal"])
         flops += acc.bwd_flops(1, heads, w["N"], 128, w["causal"])
     dt = time.perf_counter() - t0
-    del np
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(cores),
+        "cores": ORACLE_THREADS,
         "kind": "oracle",
         "sample": (f"fp64 oracle {'forward+backward' if has_bwd else 'forward'} on heads 0-{heads - 1} "
-                   f"of the same workload (batch 0), {dt:.1f} s wall; credited FLOPs of that sample"),
+                   f"of batch 0 of the same workload, {dt:.1f} s wall after a warm-up on 256 rows; "
+                   f"credited FLOPs of that sample"),
         "seconds": dt,
-        "host_cpu": platform.processor() or platform.machine(),
+        "blas_threads": max(blas, default=None),
+        "affinity_cores": len(os.sched_getaffinity(0)),
+        "host_cpu": cpu_model(),
     }
+
+
+def gpu_clocks():
+    """Current graphics (sclk) and memory (mclk) clock levels in MHz, read
+    from the driver's DPM tables (the level marked '*'), or None."""
+    out = {}
+    for card in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            if open(os.path.join(card, "vendor")).read().strip() != "0x1002":
+                continue
+            for name in ("sclk", "mclk"):
+                for line in open(os.path.join(card, f"pp_dpm_{name}")):
+                    if line.rstrip().endswith("*"):
+                        out[name + "_mhz"] = float(line.split(":")[1].strip().rstrip("*").strip()
+                                                   .lower().replace("mhz", ""))
+        except (OSError, ValueError, IndexError):
+            continue
+        if out:
+            out["source"] = card + "/pp_dpm_{sclk,mclk}"
+            return out
+    return None
+
+
+def kernel_stats(samples):
+    """mean, median and min of per-launch durations (ms)."""
+    return {"mean": sum(samples) / len(samples), "median": statistics.median(samples),
+            "min": min(samples)}
 
 
 def fp8_forward(fa, torch, q, k, v, w, workload, stream, warmup: int, steps: int):
@@ -154,7 +222,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=40,
                     help="untimed steps first; about 0.2 s lets the clocks settle")
     ap.add_argument("--workload", default="causal_b1_h64_n8192", choices=sorted(fa_inputs.WORKLOADS))
-    ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the oracle timing sample")
+    ap.add_argument("--cpu-heads", type=int, default=None,
+                    help="heads in the oracle timing sample (default: per workload, 10-30 s)")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="forward-only workloads: write this many MiB of scratch before every "
+                         "timed step, outside the timed region, so that no input is still in the "
+                         "256 MB last-level cache (0: no flush; the K steps then run as one graph)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward timing")
     ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
@@ -226,12 +299,22 @@ def main():
             if ev is not None:
                 ev[4].record(stream)
 
+    flush_bytes = (args.flush_mib << 20) if not with_bwd else 0
+    scratch = torch.empty(max(flush_bytes // 4, 1), dtype=torch.float32, device=dev)
+
+    def flush():
+        # Write more than the 256 MB last-level cache holds, so that the next
+        # step finds none of its inputs there (outside the timed region).
+        scratch.fill_(1.0)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
+    clocks_before = gpu_clocks()
 
-    use_graph = args.graph == "on" or (args.graph == "auto" and not with_bwd)
+    use_graph = args.graph == "on" or (args.graph == "auto" and not with_bwd and not flush_bytes)
+    samples = {n: [] for n in names}
     if use_graph:
         # The K steps captured once and replayed: the GPU runs them back to
         # back with no host launch work in between.  Kernel time = replay
@@ -252,20 +335,46 @@ def main():
         ev[1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        kern_ms = {"fwd": ev[0].elapsed_time(ev[1]) / args.steps}
+        samples["fwd"] = [ev[0].elapsed_time(ev[1]) / args.steps]
+        ms_per_step = wall / args.steps * 1e3
+        timing = "one HIP graph of the K steps (inputs may stay in the last-level cache)"
+    elif flush_bytes:
+        # Forward-only workloads: every timed step follows a scratch write of
+        # flush_bytes; the step's time is its own event pair, so the flush is
+        # outside it (and the flush, enqueued first, also hides the host's
+        # launch latency from these microsecond kernels).
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s_ in range(args.steps):
+            flush()
+            step(evs[s_])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        samples["fwd"] = [e[0].elapsed_time(e[1]) for e in evs]
+        ms_per_step = sum(samples["fwd"]) / args.steps
+        timing = (f"HIP events around every step, each after a {args.flush_mib} MiB scratch write "
+                  f"(outside the events); {wall / args.steps * 1e3:.3f} ms per step and flush on the "
+                  f"host clock")
     else:
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
                for _ in range(args.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for s in range(args.steps):
-            step(evs[s])
+        for s_ in range(args.steps):
+            step(evs[s_])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        kern_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
-    ms_per_step = wall / args.steps * 1e3
-    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; per kernel (ms): "
-        + ", ".join(f"{n} {t:.3f}" for n, t in kern_ms.items()))
+        for i, n in enumerate(names):
+            samples[n] = [e[i].elapsed_time(e[i + 1]) for e in evs]
+        ms_per_step = wall / args.steps * 1e3
+        timing = "HIP events around every kernel; value from the host clock around the K steps"
+    clocks_after = gpu_clocks()
+    stats = {n: kernel_stats(v_) for n, v_ in samples.items()}
+    kern_ms = {n: st["mean"] for n, st in stats.items()}
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; per kernel mean/median/min (ms): "
+        + ", ".join(f"{n} {t['mean']:.4f}/{t['median']:.4f}/{t['min']:.4f}" for n, t in stats.items()))
+    log(f"clocks before {clocks_before}, after {clocks_after}")
 
     peak = acc.MI355X_BF16_DENSE_TFLOPS
     fwd_f = acc.fwd_flops(B, H, N, d, causal)
@@ -274,7 +383,7 @@ def main():
     value = step_f / (ms_per_step * 1e-3) / 1e12
     fwd_tf = fwd_f / (kern_ms["fwd"] * 1e-3) / 1e12
     out_extra = {
-        "timing": "one HIP graph of the K steps" if use_graph else "HIP events around every kernel",
+        "timing": timing,
         "fwd_ms": kern_ms["fwd"],
         "fwd_tflops": fwd_tf,
         "fwd_frac_of_peak": fwd_tf / peak,
@@ -283,8 +392,11 @@ def main():
     if with_bwd:
         bwd_ms = kern_ms["bwd_pre"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
         bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
-        out_extra.update({"bwd_ms": bwd_ms, "bwd_tflops": bwd_tf, "bwd_frac_of_peak": bwd_tf / peak,
-                          "kernel_ms": kern_ms})
+        out_extra.update({"bwd_ms": bwd_ms, "bwd_tflops": bwd_tf, "bwd_frac_of_peak": bwd_tf / peak})
+    out_extra["kernel_ms"] = kern_ms
+    out_extra["kernel_ms_median"] = {n: st["median"] for n, st in stats.items()}
+    out_extra["kernel_ms_min"] = {n: st["min"] for n, st in stats.items()}
+    out_extra["clocks"] = {"before": clocks_before, "after": clocks_after}
 
     # Roofline of the kernel that takes the most time per step.
     half = 0.5 if causal else 1.0
@@ -319,8 +431,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"timing the fp64 oracle on {args.cpu_heads} heads ...")
-        cpu = cpu_baseline(x, w, args.cpu_heads)
+        heads = args.cpu_heads or CPU_SAMPLE_HEADS[args.workload]
+        log(f"timing the fp64 oracle on {heads} heads ({ORACLE_THREADS} BLAS threads) ...")
+        cpu = cpu_baseline(x, w, heads)
         log(f"oracle: {cpu['seconds']:.1f} s, {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
 
     line = {
@@ -335,7 +448,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic: seeded iid N(0,1) bf16 Q, K, V, dO",
+        "data": ("synthetic: seeded iid Gaussian bf16 Q, K, V" + (", dO" if with_bwd else "")
+                 + (f" (Q, K std {w['qk_std']:g})" if w["qk_std"] != 1.0 else "")),
         "config": {"workload": args.workload + ("_fwd_bwd" if with_bwd else "_fwd"), "B": B, "H": H,
                    "N": N, "d": d, "causal": causal, "scale": scale},
         "frac_of_peak": value / peak,
