@@ -9,6 +9,7 @@ Functions mirror the C entry points:
   fa_fwd(q, k, v, o, lse, scale, causal)                       -> None
   fa_fwd_split(q, k, v, o, lse, scale, causal)                 -> None
   fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale, causal, ws)   -> None
+  fa_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, scale, causal) -> None
   fa_bwd_preprocess(o, dO, lse, ws)                            -> None
   fa_bwd_dkdv(q, k, v, dO, ws, dk, dv, scale, causal)          -> None
   fa_bwd_dq(q, k, v, dO, ws, dq, scale, causal)                -> None
@@ -36,6 +37,8 @@ FA_ERR_INVALID_ARG = 1
 FA_ERR_UNSUPPORTED = 2
 FA_ERR_WORKSPACE = 3
 FA_ERR_HIP = 4
+FA_ERR_TOO_LARGE = 5
+NOALLOC_MAX_ROWS = (16 << 20) // 8   # FA_NOALLOC_MAX_ROWS of include/fa.h
 
 _lib = None
 
@@ -62,6 +65,8 @@ def load_library() -> ctypes.CDLL:
         lib.fa_bwd_workspace_size.restype = sz
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
         lib.fa_bwd.restype = i
+        lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_bwd_noalloc.restype = i
         lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, vp]
         lib.fa_bwd_preprocess.restype = i
         lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, f, i, vp]
@@ -151,6 +156,20 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, workspac
     st = load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                                _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
                                _ptr(workspace), nbytes, _stream(stream))
+    if st != FA_OK:
+        raise FAError(st)
+
+
+def fa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool,
+                   stream=None) -> None:
+    B, H, N, d = _shape(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dO", do), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        _check_tensor(name, t, torch.bfloat16, (B, H, N, d))
+    _check_tensor("lse", lse, torch.float32, (B, H, N))
+    st = load_library().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                       _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
+                                       int(bool(causal)), _stream(stream))
     if st != FA_OK:
         raise FAError(st)
 

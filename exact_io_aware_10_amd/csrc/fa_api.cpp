@@ -139,6 +139,23 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                   float scale, int causal, void* stream) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, causal, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_UNSUPPORTED;
+  if (fa_bwd_workspace_size(B, H, N, d, causal) > (size_t)FA_NOALLOC_SCRATCH_BYTES)
+    return FA_ERR_TOO_LARGE;
+  hipError_t e = fa::launch_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, scale, causal,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_fp8_codes_size(int B, int H, int N, int d, int layout) {
   bool empty = false;
   if (check_common(B, H, N, d, 1.f, 0, &empty) != FA_OK || empty) return 0;
@@ -189,6 +206,8 @@ const char* fa_strerror(int status) {
     case FA_ERR_UNSUPPORTED: return "unsupported (head dim other than 128, misaligned pointer, or size overflow)";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than fa_bwd_workspace_size()";
     case FA_ERR_HIP: return "HIP runtime rejected the launch";
+    case FA_ERR_TOO_LARGE:
+      return "problem too large for fa_bwd_noalloc's fixed scratch (B*H*N above FA_NOALLOC_MAX_ROWS)";
     default: return "unknown status";
   }
 }

@@ -18,6 +18,9 @@
 // Tiles reach LDS through LDS-direct buffer loads; rows past N read as zero,
 // which makes their P finite and their dO, dP, D and dS zero, so they add
 // nothing to any gradient.
+#include <mutex>
+
+#include "fa.h"
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -841,6 +844,48 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                      static_cast<const uint16_t*>(dO), ws, static_cast<uint16_t*>(dq), BH, N, nqb,
                      sl2, scale, sc.keep, sc.flip);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free backward (fa_bwd_noalloc): the [D | L log2(e)] workspace
+// lives in this fixed device array, one copy per GPU, held until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in): the device address of each GPU's copy is looked up
+// once per device with hipGetSymbolAddress, with that device current, and
+// kept here.  Nothing in it needs clearing: the pre-pass writes every entry
+// the dK/dV and dQ kernels then read.  Calls that overlap on one GPU share
+// the array and race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+}  // namespace
+
+hipError_t launch_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                              const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                              int B, int H, int N, float scale, int causal, hipStream_t stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_addr[dev] == nullptr) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      g_scratch_addr[dev] = p;
+    }
+    ws = static_cast<float*>(g_scratch_addr[dev]);
+  }
+  e = launch_bwd_pre(o, dO, lse, ws, B, H, N, stream);
+  if (e == hipSuccess) e = launch_bwd_dkdv(q, k, v, dO, ws, dk, dv, B, H, N, scale, causal, stream);
+  if (e == hipSuccess) e = launch_bwd_dq(q, k, v, dO, ws, dq, B, H, N, scale, causal, stream);
+  return e;
 }
 
 }  // namespace fa

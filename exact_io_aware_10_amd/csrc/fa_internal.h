@@ -51,6 +51,12 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
                          const float* ws, void* dq, int B, int H, int N, float scale, int causal,
                          hipStream_t stream);
 
+// The backward with its workspace in the library's fixed per-GPU scratch
+// array (fa_bwd.hip); the caller has checked the size against it.
+hipError_t launch_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                              const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                              int B, int H, int N, float scale, int causal, hipStream_t stream);
+
 // FP8 path (fa_fp8.hip).
 hipError_t launch_fp8_quant(const void* x, const float* signs, void* codes, int* exps, int B, int H,
                             int N, int layout, hipStream_t stream);

@@ -50,7 +50,8 @@ typedef enum {
   FA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, non-finite scale, bad causal */
   FA_ERR_UNSUPPORTED = 2,  /* d != 128, misaligned pointer, size overflow */
   FA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
-  FA_ERR_HIP = 4           /* the HIP runtime rejected a launch */
+  FA_ERR_HIP = 4,          /* the HIP runtime rejected a launch */
+  FA_ERR_TOO_LARGE = 5     /* fa_bwd_noalloc: B*H*N above FA_NOALLOC_MAX_ROWS */
 } fa_status;
 
 /*
@@ -109,6 +110,25 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            const float* lse, void* dq, void* dk, void* dv,
            int B, int H, int N, int d, float scale, int causal,
            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The backward pass without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, outputs, results
+ * (bitwise those of fa_bwd) and error behaviour as fa_bwd, minus the
+ * workspace.  It calls no allocator: the [D | L*log2(e)] workspace lives in a
+ * fixed array inside the library, FA_NOALLOC_SCRATCH_BYTES per GPU, which
+ * each GPU the library runs on holds until the process ends.  Problems whose
+ * workspace would not fit (B*H*N above FA_NOALLOC_MAX_ROWS) are rejected with
+ * FA_ERR_TOO_LARGE before anything is launched.  All calls on one GPU share
+ * that GPU's array: calls that may overlap on one GPU (different streams or
+ * threads without ordering between them) race and must not be issued.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+#define FA_NOALLOC_MAX_ROWS (FA_NOALLOC_SCRATCH_BYTES / 8u)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
  * The three stages fa_bwd runs, in order, on one stream.  Each is exposed so a

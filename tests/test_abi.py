@@ -39,9 +39,10 @@ def test_library_exports_every_declared_symbol(fa):
 
 
 def test_status_strings(fa):
-    for st in range(5):
+    for st in range(6):
         assert fa.fa_strerror(st)
     assert "unknown" in fa.fa_strerror(99)
+    assert "noalloc" in fa.fa_strerror(fa.FA_ERR_TOO_LARGE)
 
 
 def test_workspace_size(fa):
@@ -166,3 +167,20 @@ def test_missing_library_fails_loudly():
             "    print('raised:', e)\n")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 0 and "raised:" in r.stdout and "missing" in r.stdout
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(fa):
+    """fa_bwd_noalloc's fixed scratch holds the workspace of at most
+    FA_NOALLOC_MAX_ROWS rows (B*H*N); one row more is rejected before any
+    launch.  Its other argument checks are fa_bwd's."""
+    lib = fa.load_library()
+    p = [FAKE] * 9
+    assert fa.NOALLOC_MAX_ROWS == 2097152
+    assert lib.fa_bwd_noalloc(*p, 1, 1, fa.NOALLOC_MAX_ROWS + 1, 128, 0.1, 1, None) == fa.FA_ERR_TOO_LARGE
+    assert lib.fa_bwd_noalloc(*p, 2, 4, fa.NOALLOC_MAX_ROWS // 8 + 1, 128, 0.1, 0, None) == fa.FA_ERR_TOO_LARGE
+    assert lib.fa_bwd_noalloc(*p, 1, 1, 16, 64, 0.1, 0, None) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_bwd_noalloc(*p, 1, 1, 16, 128, float("nan"), 0, None) == fa.FA_ERR_INVALID_ARG
+    q = list(p)
+    q[4] = None
+    assert lib.fa_bwd_noalloc(*q, 1, 1, 16, 128, 0.1, 0, None) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_bwd_noalloc(*([None] * 9), 1, 0, 16, 128, 0.1, 0, None) == fa.FA_OK
