@@ -477,10 +477,11 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 // stream through a four-slot LDS ring.  Owning 64 queries lets every K or V
 // fragment read from LDS feed two MFMAs.  Per tile t and wave:
 //   A  S^T  = K_t Q^T      16 MFMAs (VGPR accumulators, inline assembly)
-//   B  dP^T = V_t dO^T     16 MFMAs, interleaved with P = exp2(S scale log2 e
-//                          - L log2 e) of tile t
+//   B  dP^T - D = V_t dO^T - D   16 MFMAs (the chain starts from -D of the
+//                          lane's query), interleaved with P = exp2(S scale
+//                          log2 e - L log2 e) of tile t
 //   C  dQ^T += K_{t-1}^T dS_{t-1}^T   16 MFMAs, interleaved with
-//                          dS = P (dP - D) of tile t, packed to bf16
+//                          dS = P (dP - D) of tile t (one multiply), packed to bf16
 // ---------------------------------------------------------------------------
 constexpr int DQ_QW = 64;                    // queries per wave
 constexpr int DQ_WAVES = 4;
@@ -502,6 +503,11 @@ __device__ __forceinline__ void mfma_va0(f32x16& c, bf16x8 a, const bf16x8& b) {
 }
 __device__ __forceinline__ void mfma_va(f32x16& c, bf16x8 a, const bf16x8& b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b) : "memory");
+}
+// dP^T MFMA started from the accumulator c0 (not written while the chain
+// runs) instead of zero; hazards as for mfma_v.
+__device__ __forceinline__ void mfma_v_from(f32x16& c, bf16x8 a, bf16x8 b, const f32x16& c0) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(c) : "v"(a), "v"(b), "v"(c0) : "memory");
 }
 // dQ^T += A B with the accumulator in AGPRs (fenced by acc_fence8).
 __device__ __forceinline__ void mfma_aa(f32x16& c, bf16x8 a, bf16x8 b) {
@@ -578,6 +584,13 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   // Wait for L and D here, in the compiler's view as well, before any
   // LDS-direct load (invisible to it) is in flight.
   asm volatile("" : : "v"(l2[0]), "v"(l2[1]), "v"(dd[0]), "v"(dd[1]));
+  // -D of the lane's query in every element: the dP^T chain starts from it,
+  // so that its MFMAs produce dP - D and dS = P (dP - D) is one multiply.
+  f32x16 ndd[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ndd[g][i] = -dd[g];
 
   // Tiles the workgroup streams, and tiles this wave computes on.
   const int kend = CAUSAL ? min(N, q0 + DQ_BQ) : N;
@@ -735,7 +748,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         if (kc == 0)
-          mfma_v_init(dp[g], va[b], df[g][kc]);
+          mfma_v_from(dp[g], va[b], df[g][kc], ndd[g]);
         else
           mfma_v(dp[g], va[b], df[g][kc]);
         const int idx = 2 * (2 * kc + g);  // scores idx, idx + 1 of the 32
@@ -756,8 +769,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     dq_products(PSL, [&](int m) {
       const int idx = 2 * m;
       const int sg = idx >> 4, si = idx & 15;
-      const float d0 = s[sg][si] * (dp[sg][si] - dd[sg]);
-      const float d1 = s[sg][si + 1] * (dp[sg][si + 1] - dd[sg]);
+      const float d0 = s[sg][si] * dp[sg][si];  // dp holds dP - D
+      const float d1 = s[sg][si + 1] * dp[sg][si + 1];
       w[sg][si >> 1] = pack_bf16(d0, d1);
       asm volatile("" : "+v"(w[sg][si >> 1]));  // convert here, not after the loop
     });
