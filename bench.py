@@ -233,6 +233,11 @@ def main():
     ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
                     help="time the K steps as one HIP graph replay (auto: for forward-only "
                          "workloads, whose microsecond kernels would otherwise wait on the host)")
+    ap.add_argument("--operands", choices=("gaussian", "constant"), default="gaussian",
+                    help="constant: every input element 0.5 instead of the workload's Gaussian "
+                         "draws -- a diagnostic of how much the operands' switching activity "
+                         "costs at the power cap (same instructions, same shapes); not the "
+                         "metric's inputs, and the oracle baseline is skipped")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -266,6 +271,10 @@ def main():
     log(f"workload {args.workload}: B={B} H={H} N={N} d={d} causal={causal} bwd={with_bwd}")
 
     x = fa_inputs.make_workload(args.workload, with_do=with_bwd)
+    if args.operands == "constant":
+        import numpy as np
+        x = {n: np.full_like(a, 0x3F00) for n, a in x.items()}  # bf16 bits of 0.5
+        args.no_cpu_baseline = True
     dev = torch.device("cuda:0")
 
     def put(bits):
@@ -449,7 +458,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": ("synthetic: seeded iid Gaussian bf16 Q, K, V" + (", dO" if with_bwd else "")
-                 + (f" (Q, K std {w['qk_std']:g})" if w["qk_std"] != 1.0 else "")),
+                 + (f" (Q, K std {w['qk_std']:g})" if w["qk_std"] != 1.0 else "")
+                 if args.operands == "gaussian" else
+                 "diagnostic: every input element 0.5 (not the metric's inputs)"),
         "config": {"workload": args.workload + ("_fwd_bwd" if with_bwd else "_fwd"), "B": B, "H": H,
                    "N": N, "d": d, "causal": causal, "scale": scale},
         "frac_of_peak": value / peak,

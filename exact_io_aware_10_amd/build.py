@@ -55,6 +55,22 @@ def _check_asm(src: str) -> None:
         raise RuntimeError(f"{src}: inline-asm MFMA results read too early:\n" + "\n".join(problems))
 
 
+MICRO_SRC = os.path.join(ROOT, "micro", "micro.hip")
+MICRO_BIN = os.path.join(ROOT, "micro", "micro")
+
+
+def build_micro(verbose: bool = False) -> str:
+    """The microbenchmark program (micro/micro.hip) behind the rates the kernels'
+    design relies on; a standalone executable, not part of the library."""
+    cmd = [HIPCC, *COMMON, "-munsafe-fp-atomics", MICRO_SRC, "-o", MICRO_BIN]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for micro.hip:\n{r.stderr}")
+    if verbose:
+        print(f"built {MICRO_BIN}")
+    return MICRO_BIN
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
@@ -73,4 +89,5 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_micro(verbose=True)
     sys.exit(0)

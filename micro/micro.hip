@@ -1,0 +1,390 @@
+// Microbenchmarks of the gfx950 rates the attention kernels' design rests on.
+//
+//   mfma     bf16 32x32x16 MFMA throughput, four independent accumulators
+//            per wave, two waves per SIMD, with operands of random bits
+//            (a different fragment for every MFMA of the loop) or constant
+//            (every fragment 1.0): the chip runs at its power cap, and the
+//            switching activity of the operands sets the clock it can hold.
+//   valu     cycles per wave64 instruction of v_fma_f32 and v_exp_f32 (16
+//            independent chains per wave; core cycles from s_memtime).
+//   coexec   an MFMA stream and a VALU stream (exp + fma, as in a softmax):
+//            each alone, one of each on every SIMD (two waves), and both in
+//            one wave, interleaved.
+//   atomic   fp32 global atomic add bandwidth: every lane adds one float,
+//            rows of 256 bytes per wave, all to distinct addresses.
+//
+// Every kernel writes only through vector stores, every access is to a
+// buffer sized on the host for exactly the grid launched, and every loop
+// has a fixed trip count.  Prints one JSON line per measurement.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#define CHECK(x)                                                                      \
+  do {                                                                                \
+    hipError_t e_ = (x);                                                              \
+    if (e_ != hipSuccess) {                                                           \
+      fprintf(stderr, "HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__); \
+      exit(1);                                                                        \
+    }                                                                                 \
+  } while (0)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCUs = 256;
+
+// ---------------------------------------------------------------------------
+// MFMA throughput.  src holds 8 fragments (16 bytes per lane) per lane of a
+// 256-thread block: fragments 0-3 are A operands, 4-7 B operands.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mfma_rate(const u32x4* __restrict__ src, float* __restrict__ out,
+                                                 int iters) {
+  const int tid = threadIdx.x;
+  bf16x8 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = __builtin_bit_cast(bf16x8, src[i * 256 + tid]);
+    b[i] = __builtin_bit_cast(bf16x8, src[(4 + i) * 256 + tid]);
+  }
+  f32x16 c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) c[i][j] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[i ^ 1], c[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i ^ 2], b[i ^ 3], c[i], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += c[i][j];
+  out[blockIdx.x * 256 + tid] = s;
+}
+
+// ---------------------------------------------------------------------------
+// VALU: 16 independent chains of one instruction kind per wave; out gets the
+// core cycles the loop took (s_memtime) and a checksum.
+// ---------------------------------------------------------------------------
+template <int KIND>  // 0: v_fma_f32, 1: v_exp_f32
+__global__ __launch_bounds__(256) void valu_rate(float* __restrict__ out, long long* __restrict__ cyc,
+                                                 int iters) {
+  const int tid = threadIdx.x;
+  float f[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) f[j] = 0.001f * tid + 0.01f * j - 0.5f;
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (KIND == 0)
+        f[j] = __builtin_fmaf(f[j], 0.999f, 0.0001f);
+      else
+        f[j] = __builtin_amdgcn_exp2f(f[j]) - 1.0f;  // stays in (-1, 1): exp2 then one add
+      asm volatile("" : "+v"(f[j]));
+    }
+  }
+  const long long t1 = __builtin_amdgcn_s_memtime();
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s += f[j];
+  out[blockIdx.x * 256 + tid] = s;
+  if ((tid & 63) == 0) cyc[blockIdx.x * 4 + (tid >> 6)] = t1 - t0;
+}
+
+// ---------------------------------------------------------------------------
+// One wave per SIMD: the same 16 exp2(fma(x)) pairs per iteration, issued
+// either back to back (each exp right after the fma it reads: ORDER 0) or
+// software-pipelined (the fma of the next pair between an fma and its exp:
+// ORDER 1).  A wave alone on its SIMD has no other wave to fill the cycles a
+// dependent instruction waits for its input.
+// ---------------------------------------------------------------------------
+template <int ORDER>
+__global__ __launch_bounds__(256) void valu_dep(float* __restrict__ out, long long* __restrict__ cyc,
+                                                int iters) {
+  const int tid = threadIdx.x;
+  float f[16], x[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) f[j] = 0.001f * tid + 0.01f * j - 0.5f;
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+    if (ORDER == 0) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        x[j] = __builtin_fmaf(f[j], 0.5f, -0.25f);
+        asm volatile("" : "+v"(x[j]));
+        f[j] = __builtin_amdgcn_exp2f(x[j]);
+        asm volatile("" : "+v"(f[j]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      x[0] = __builtin_fmaf(f[0], 0.5f, -0.25f);
+      asm volatile("" : "+v"(x[0]));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (j + 1 < 16) {
+          x[j + 1] = __builtin_fmaf(f[j + 1], 0.5f, -0.25f);
+          asm volatile("" : "+v"(x[j + 1]));
+        }
+        f[j] = __builtin_amdgcn_exp2f(x[j]);
+        asm volatile("" : "+v"(f[j]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  const long long t1 = __builtin_amdgcn_s_memtime();
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s += f[j];
+  out[blockIdx.x * 256 + tid] = s;
+  if ((tid & 63) == 0) cyc[blockIdx.x * 4 + (tid >> 6)] = t1 - t0;
+}
+
+// ---------------------------------------------------------------------------
+// Co-execution, 512 threads (8 waves) per block, one block per CU: waves w
+// and w + 4 share a SIMD.  MODE 0: waves 0-3 run the MFMA stream (4 x 8
+// MFMAs per iteration), 4-7 idle; 1: waves 4-7 run the VALU stream (per
+// iteration 32 exp2 + 32 fma, a softmax's share per 64-key tile), 0-3 idle;
+// 2: both (one of each per SIMD); 3: waves 0-3 run both streams interleaved
+// in one instruction stream, 4-7 idle.
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ __launch_bounds__(512) void coexec(const u32x4* __restrict__ src, float* __restrict__ out,
+                                              long long* __restrict__ cyc, int iters) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const bool mwave = wave < 4;
+  const bool do_mfma = mwave && (MODE == 0 || MODE == 2 || MODE == 3);
+  const bool do_valu = (MODE == 3) ? mwave : (!mwave && (MODE == 1 || MODE == 2));
+  const int t = tid & 255;
+  bf16x8 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = __builtin_bit_cast(bf16x8, src[i * 256 + t]);
+    b[i] = __builtin_bit_cast(bf16x8, src[(4 + i) * 256 + t]);
+  }
+  f32x16 c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) c[i][j] = 0.f;
+  float f[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) f[j] = 0.001f * t + 0.01f * j - 0.5f;
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  if (do_mfma && do_valu) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        c[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i & 3], b[(i + 1) & 3], c[i & 3], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int k = 4 * i + j;
+          f[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[k], 0.5f, -0.25f));
+          asm volatile("" : "+v"(f[k]));
+        }
+      }
+    }
+  } else if (do_mfma) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        c[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i & 3], b[(i + 1) & 3], c[i & 3], 0, 0, 0);
+    }
+  } else if (do_valu) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        f[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[k], 0.5f, -0.25f));
+        asm volatile("" : "+v"(f[k]));
+      }
+    }
+  }
+  const long long t1 = __builtin_amdgcn_s_memtime();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += c[i][j];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) s += f[j];
+  out[blockIdx.x * 512 + tid] = s;
+  if ((tid & 63) == 0) cyc[blockIdx.x * 8 + wave] = (do_mfma || do_valu) ? (t1 - t0) : 0;
+}
+
+// ---------------------------------------------------------------------------
+// fp32 atomic add bandwidth: thread g adds 1.0 to dst[(g + it * threads) %
+// n] for it < iters (n a multiple of the thread count, so every index is in
+// bounds and a wave's 64 adds cover one 256-byte row).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void atomic_rate(float* __restrict__ dst, int n, int iters) {
+  const int threads = gridDim.x * 256;
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  for (int it = 0; it < iters; ++it) {
+    const int idx = (int)(((long long)g + (long long)it * threads) % n);
+    __hip_atomic_fetch_add(dst + idx, 1.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ---------------------------------------------------------------------------
+static unsigned lcg(unsigned& s) {
+  s = s * 1664525u + 1013904223u;
+  return s;
+}
+
+static float time_ms(hipEvent_t e0, hipEvent_t e1) {
+  float ms = 0.f;
+  CHECK(hipEventElapsedTime(&ms, e0, e1));
+  return ms;
+}
+
+int main(int argc, char** argv) {
+  const char* only = argc > 1 ? argv[1] : "";
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+
+  // Operand fragments: 8 per lane x 256 lanes, 16 bytes each.
+  const int nfrag = 8 * 256;
+  std::vector<unsigned> rnd(nfrag * 4), one(nfrag * 4, 0x3f803f80u);
+  unsigned seed = 12345u;
+  for (auto& x : rnd) {
+    // random bf16 pairs with exponents in [-8, 7] (finite, no overflow in the sums)
+    unsigned lo = (lcg(seed) & 0x807fu) | ((120u + (lcg(seed) % 16u)) << 7);
+    unsigned hi = (lcg(seed) & 0x807fu) | ((120u + (lcg(seed) % 16u)) << 7);
+    x = lo | (hi << 16);
+  }
+  u32x4* src;
+  CHECK(hipMalloc(&src, nfrag * 16));
+  const int blocks = 2 * kCUs * 4;  // 4 blocks of 4 waves per CU, 4 waves per SIMD over the run
+  float* out;
+  CHECK(hipMalloc(&out, (size_t)blocks * 512 * sizeof(float)));
+  long long* cyc;
+  CHECK(hipMalloc(&cyc, (size_t)blocks * 8 * sizeof(long long)));
+  std::vector<long long> hc((size_t)blocks * 8);
+
+  if (!*only || !strcmp(only, "mfma")) {
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int rnd_ops = 1; rnd_ops >= 0; --rnd_ops) {
+        CHECK(hipMemcpy(src, rnd_ops ? rnd.data() : one.data(), nfrag * 16, hipMemcpyHostToDevice));
+        const int iters = 20000;
+        const int grid = 2 * kCUs;  // two blocks of four waves per CU: two waves per SIMD
+        hipLaunchKernelGGL(mfma_rate, dim3(grid), dim3(256), 0, 0, src, out, 100);
+        CHECK(hipDeviceSynchronize());
+        CHECK(hipEventRecord(e0));
+        hipLaunchKernelGGL(mfma_rate, dim3(grid), dim3(256), 0, 0, src, out, iters);
+        CHECK(hipEventRecord(e1));
+        CHECK(hipDeviceSynchronize());
+        const double ms = time_ms(e0, e1);
+        const double flop = (double)grid * 4 * iters * 8 * 32.0 * 32 * 16 * 2;
+        if (pass)
+          printf("{\"probe\": \"mfma_bf16_32x32x16\", \"operands\": \"%s\", \"ms\": %.3f, \"tflops\": %.1f}\n",
+                 rnd_ops ? "random" : "constant", ms, flop / ms / 1e9);
+      }
+    }
+  }
+  if (!*only || !strcmp(only, "valu")) {
+    for (int kind = 0; kind < 2; ++kind) {
+      const int iters = 4000;
+      const int grid = 2 * kCUs;
+      for (int w = 0; w < 2; ++w) {
+        if (kind == 0)
+          hipLaunchKernelGGL(valu_rate<0>, dim3(grid), dim3(256), 0, 0, out, cyc, iters);
+        else
+          hipLaunchKernelGGL(valu_rate<1>, dim3(grid), dim3(256), 0, 0, out, cyc, iters);
+        CHECK(hipDeviceSynchronize());
+      }
+      CHECK(hipMemcpy(hc.data(), cyc, (size_t)grid * 4 * sizeof(long long), hipMemcpyDeviceToHost));
+      double avg = 0;
+      for (int i = 0; i < grid * 4; ++i) avg += (double)hc[i];
+      avg /= grid * 4;
+      // two waves per SIMD share its issue: cycles per instruction of one wave / 2 = SIMD cost
+      printf("{\"probe\": \"valu\", \"instruction\": \"%s\", \"waves_per_simd\": 2, "
+             "\"core_cycles_per_wave_instruction\": %.2f, \"simd_cycles_per_instruction\": %.2f}\n",
+             kind == 0 ? "v_fma_f32" : "v_exp_f32 + v_add_f32", avg / (iters * 16.0), avg / (iters * 16.0) / 2);
+    }
+  }
+  if (!*only || !strcmp(only, "valu1")) {
+    for (int order = 0; order < 2; ++order) {
+      const int iters = 4000;
+      const int grid = kCUs;  // one block of four waves per CU: one wave per SIMD
+      for (int w = 0; w < 2; ++w) {
+        if (order == 0)
+          hipLaunchKernelGGL(valu_dep<0>, dim3(grid), dim3(256), 0, 0, out, cyc, iters);
+        else
+          hipLaunchKernelGGL(valu_dep<1>, dim3(grid), dim3(256), 0, 0, out, cyc, iters);
+        CHECK(hipDeviceSynchronize());
+      }
+      CHECK(hipMemcpy(hc.data(), cyc, (size_t)grid * 4 * sizeof(long long), hipMemcpyDeviceToHost));
+      double avg = 0;
+      for (int i = 0; i < grid * 4; ++i) avg += (double)hc[i];
+      avg /= grid * 4;
+      printf("{\"probe\": \"valu_one_wave_per_simd\", \"order\": \"%s\", \"core_cycles_per_fma_exp_pair\": %.2f}\n",
+             order == 0 ? "exp right after its fma" : "next fma between fma and exp", avg / (iters * 16.0));
+    }
+  }
+  if (!*only || !strcmp(only, "coexec")) {
+    CHECK(hipMemcpy(src, rnd.data(), nfrag * 16, hipMemcpyHostToDevice));
+    const char* names[4] = {"mfma stream alone", "valu stream alone", "one mfma wave + one valu wave per simd",
+                            "both streams in one wave"};
+    const int iters = 2000;
+    const int grid = kCUs;
+    for (int mode = 0; mode < 4; ++mode) {
+      for (int w = 0; w < 2; ++w) {
+        switch (mode) {
+          case 0: hipLaunchKernelGGL(coexec<0>, dim3(grid), dim3(512), 0, 0, src, out, cyc, iters); break;
+          case 1: hipLaunchKernelGGL(coexec<1>, dim3(grid), dim3(512), 0, 0, src, out, cyc, iters); break;
+          case 2: hipLaunchKernelGGL(coexec<2>, dim3(grid), dim3(512), 0, 0, src, out, cyc, iters); break;
+          default: hipLaunchKernelGGL(coexec<3>, dim3(grid), dim3(512), 0, 0, src, out, cyc, iters); break;
+        }
+        CHECK(hipDeviceSynchronize());  // the first launch warms up; the second's cycles are kept
+      }
+      CHECK(hipMemcpy(hc.data(), cyc, (size_t)grid * 8 * sizeof(long long), hipMemcpyDeviceToHost));
+      // waves 0-3 of each block vs waves 4-7 (the MFMA and VALU waves in mode 2)
+      double sum[2] = {0, 0};
+      int cnt[2] = {0, 0};
+      for (int i = 0; i < grid * 8; ++i)
+        if (hc[i] > 0) {
+          const int grp = (i % 8) >= 4;
+          sum[grp] += (double)hc[i];
+          ++cnt[grp];
+        }
+      printf("{\"probe\": \"coexec\", \"mode\": \"%s\", \"core_cycles_per_iteration_waves_0_3\": %.1f, "
+             "\"core_cycles_per_iteration_waves_4_7\": %.1f, \"mfma_cycles_per_iteration\": %d, "
+             "\"valu_per_iteration\": \"32 exp2 + 32 fma\"}\n",
+             names[mode], cnt[0] ? sum[0] / cnt[0] / iters : 0.0, cnt[1] ? sum[1] / cnt[1] / iters : 0.0, 8 * 32);
+    }
+  }
+  if (!*only || !strcmp(only, "atomic")) {
+    const int grid = 4 * kCUs;
+    const int threads = grid * 256;
+    const int n = threads * 16;  // 16 MiB of floats, a multiple of the thread count
+    const int iters = 64;
+    float* dst;
+    CHECK(hipMalloc(&dst, (size_t)n * sizeof(float)));
+    CHECK(hipMemset(dst, 0, (size_t)n * sizeof(float)));
+    hipLaunchKernelGGL(atomic_rate, dim3(grid), dim3(256), 0, 0, dst, n, 4);
+    CHECK(hipDeviceSynchronize());
+    CHECK(hipEventRecord(e0));
+    hipLaunchKernelGGL(atomic_rate, dim3(grid), dim3(256), 0, 0, dst, n, iters);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipDeviceSynchronize());
+    const double ms = time_ms(e0, e1);
+    const double bytes = (double)threads * iters * 4;
+    printf("{\"probe\": \"atomic_add_f32\", \"ms\": %.3f, \"gbps\": %.1f}\n", ms, bytes / ms / 1e6);
+    CHECK(hipFree(dst));
+  }
+  CHECK(hipFree(src));
+  CHECK(hipFree(out));
+  CHECK(hipFree(cyc));
+  return 0;
+}
