@@ -10,11 +10,13 @@
 // contribution to the Q, K and V gradients).
 //
 // Three launches, no atomics (bitwise deterministic):
-//   bwd_pre   workspace <- [D = rowsum(dO o O) | L log2(e)]   HBM-bound
+//   bwd_pre   workspace <- [-D = -rowsum(dO o O) | L log2(e)]   HBM-bound
 //   bwd_dkdv  per key block: K in registers, V in LDS; query tiles of Q, dO,
-//             L log2(e), D stream through LDS; dV^T += dO^T P, dK^T += Q^T dS
-//   bwd_dq    per query block: Q, dO, L, D held in registers; K, V tiles
+//             L log2(e), -D stream through LDS; dV^T += dO^T P, dK^T += Q^T dS
+//   bwd_dq    per query block: Q, dO, L, -D held in registers; K, V tiles
 //             stream through LDS; dQ^T += K^T dS^T
+// Both kernels start each dP accumulation chain from -D instead of zero, so
+// their MFMAs produce dP - D and dS = P (dP - D) costs one multiply.
 // Tiles reach LDS through LDS-direct buffer loads; rows past N read as zero,
 // which makes their P finite and their dO, dP, D and dS zero, so they add
 // nothing to any gradient.
@@ -46,12 +48,17 @@ __device__ __forceinline__ void mfma_v_init(f32x16& c, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mfma_v(f32x16& c, bf16x8 a, bf16x8 b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b) : "memory");
 }
+// The first MFMA of a chain started from c0 instead of zero; c0 must stay
+// unwritten for a few wait states after it (the matrix core reads it late).
+__device__ __forceinline__ void mfma_v_from(f32x16& c, bf16x8 a, bf16x8 b, const f32x16& c0) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(c) : "v"(a), "v"(b), "v"(c0) : "memory");
+}
 __device__ __forceinline__ void mfma_v_fence(f32x16& c0, f32x16& c1, f32x16& c2, f32x16& c3) {
   asm volatile("s_nop 15" : "+v"(c0), "+v"(c1), "+v"(c2), "+v"(c3));
 }
 
 // ---------------------------------------------------------------------------
-// Pre-pass: D_i = sum_k dO_ik O_ik and L_i log2(e), 16 threads per row.
+// Pre-pass: -D_i = -sum_k dO_ik O_ik and L_i log2(e), 16 threads per row.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                       const uint16_t* __restrict__ dO,
@@ -76,7 +83,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int w = 8; w >= 1; w >>= 1) s += __shfl_xor(s, w, 16);
   if (row < rows && part == 0) {
-    ws[row] = s;
+    ws[row] = -s;
     ws[(size_t)rows + row] = lse[row] * kLog2e;
   }
 }
@@ -87,7 +94,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // One wave per SIMD, four waves per workgroup: wave w owns keys
 // k0 + 64 w .. + 63 as two groups of 32.  Its K fragments stay in registers
 // for the whole kernel and the workgroup's V block sits in LDS; 32-query
-// tiles of Q, dO, L log2(e) and D stream through a four-slot LDS ring.
+// tiles of Q, dO, L log2(e) and -D stream through a four-slot LDS ring.
 // Owning 64 keys lets each Q / dO fragment read from LDS feed two MFMAs.
 // The accumulators dK^T, dV^T (256 registers) live in AGPRs; S and dP are
 // computed by VGPR-accumulator MFMAs (mfma_v) so that the softmax can read
@@ -103,7 +110,7 @@ constexpr int KV_TLOADS = KV_TILE / 1024 / KV_WAVES;  // LDS-direct loads per wa
 constexpr int KV_VLOADS = KV_VBLK / 1024 / KV_WAVES;
 // LDS layout: the ring's Q / dO tiles first, so that every constant offset
 // into them fits the 16-bit offset field of LDS instructions (no address
-// adds); then per slot four 64-entry float arrays (L log2(e), D, and two
+// adds); then per slot four 64-entry float arrays (L log2(e), -D, and two
 // sinks: the 4-byte LDS-direct load writes one entry per lane, and every wave
 // issues one so that all waves issue the same number of loads); then the V
 // block, addressed from a base register.
@@ -318,7 +325,18 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       tro[mb][1] = tr1 ^ (64 * mb);
     }
 
-    // S = Q K^T and dP = dO V^T, operands one k-step ahead.
+    // S = Q K^T and dP - D = dO V^T - D, operands one k-step ahead.  The dP
+    // chains start from -D of each element's query (the tile's -D array holds
+    // it at the same positions the accumulator tuple does: 4 (i / 4) entries
+    // apart, 4 h + i % 4 in), the same for both key groups.
+    const float* db = reinterpret_cast<const float*>(smem + dsl);
+    f32x16 nd;
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(db + 8 * gg + 4 * h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nd[4 * gg + j] = d4[j];
+    }
     f32x16 s[2], dp[2];
     bf16x8 qa[2], da[2], va[2][2];
     auto rd = [&](int kc, int b) {
@@ -336,15 +354,18 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       if (kc < 7) rd(kc + 1, b ^ 1);
       if (kc == 0) {
         mfma_v_init(s[0], qa[b], kf[0][kc]);
-        mfma_v_init(dp[0], da[b], va[b][0]);
+        mfma_v_from(dp[0], da[b], va[b][0], nd);
         mfma_v_init(s[1], qa[b], kf[1][kc]);
-        mfma_v_init(dp[1], da[b], va[b][1]);
+        mfma_v_from(dp[1], da[b], va[b][1], nd);
       } else {
         mfma_v(s[0], qa[b], kf[0][kc]);
         mfma_v(dp[0], da[b], va[b][0]);
         mfma_v(s[1], qa[b], kf[1][kc]);
         mfma_v(dp[1], da[b], va[b][1]);
       }
+      // The matrix core reads nd for a while after the MFMAs issue: keep its
+      // registers from reuse until the next k-step's MFMAs have issued.
+      if (kc == 1) asm volatile("" : : "v"(nd));
     }
     mfma_v_fence(s[0], s[1], dp[0], dp[1]);
 
@@ -367,11 +388,10 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     // n (4 MFMAs) carries the softmax of row group n / 2, key group n % 2,
     // one element per MFMA; sched_barrier keeps the compiler to that order.
     const float* lb = reinterpret_cast<const float*>(smem + lsl);
-    const float* db = reinterpret_cast<const float*>(smem + dsl);
     const int pq = psl * KV_SLOT, po = pq + KV_TILE;
     bf16x8 npb[2][2], nsb[2][2];
     bf16x8 a_do[2], a_q[2];
-    f32x4 l4[2], d4[2];
+    f32x4 l4[2];
     auto rdt = [&](int n, int b) {
       const int mb = n >> 1, ro2 = 16 * (n & 1) * kRowBytes;
       a_do[b] = join(lds_read_tr(smem + po + ro2 + tro[mb][0]), lds_read_tr(smem + po + ro2 + tro[mb][1]));
@@ -380,7 +400,6 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     auto rdl = [&](int gg) {
       const int r = 8 * gg + 4 * h;
       l4[gg & 1] = *reinterpret_cast<const f32x4*>(lb + r);
-      d4[gg & 1] = *reinterpret_cast<const f32x4*>(db + r);
     };
     rdt(0, 0);
     rdl(0);
@@ -402,7 +421,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         const int i = 4 * gg + k;
         const float p = fast_exp2(__builtin_fmaf(s[g][i], sl2, -l4[gg & 1][k]));
         s[g][i] = p;
-        dp[g][i] = p * (dp[g][i] - d4[gg & 1][k]);
+        dp[g][i] = p * dp[g][i];  // dp holds dP - D
         __builtin_amdgcn_sched_barrier(0);
       }
       // Rows 8 v .. 8 v + 7 of key group g are done after row group 2 v + 1.
@@ -504,11 +523,6 @@ __device__ __forceinline__ void mfma_va0(f32x16& c, bf16x8 a, const bf16x8& b) {
 __device__ __forceinline__ void mfma_va(f32x16& c, bf16x8 a, const bf16x8& b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b) : "memory");
 }
-// dP^T MFMA started from the accumulator c0 (not written while the chain
-// runs) instead of zero; hazards as for mfma_v.
-__device__ __forceinline__ void mfma_v_from(f32x16& c, bf16x8 a, bf16x8 b, const f32x16& c0) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(c) : "v"(a), "v"(b), "v"(c0) : "memory");
-}
 // dQ^T += A B with the accumulator in AGPRs (fenced by acc_fence8).
 __device__ __forceinline__ void mfma_aa(f32x16& c, bf16x8 a, bf16x8 b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
@@ -575,22 +589,22 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       const bf16x8 qv = __builtin_bit_cast(bf16x8, signed_operand(qraw[g][kc], qkeep, qflip));
       asm volatile("" : "=a"(qf[g][kc]) : "0"(qv));
     }
-  float l2[2], dd[2];
+  float l2[2], nd[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     l2[g] = buf_load_f32(rL, (uint32_t)(q0w + 32 * g + col) * 4);
-    dd[g] = buf_load_f32(rD, (uint32_t)(q0w + 32 * g + col) * 4);
+    nd[g] = buf_load_f32(rD, (uint32_t)(q0w + 32 * g + col) * 4);  // -D
   }
-  // Wait for L and D here, in the compiler's view as well, before any
+  // Wait for L and -D here, in the compiler's view as well, before any
   // LDS-direct load (invisible to it) is in flight.
-  asm volatile("" : : "v"(l2[0]), "v"(l2[1]), "v"(dd[0]), "v"(dd[1]));
+  asm volatile("" : : "v"(l2[0]), "v"(l2[1]), "v"(nd[0]), "v"(nd[1]));
   // -D of the lane's query in every element: the dP^T chain starts from it,
   // so that its MFMAs produce dP - D and dS = P (dP - D) is one multiply.
   f32x16 ndd[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ndd[g][i] = -dd[g];
+    for (int i = 0; i < 16; ++i) ndd[g][i] = nd[g];
 
   // Tiles the workgroup streams, and tiles this wave computes on.
   const int kend = CAUSAL ? min(N, q0 + DQ_BQ) : N;
@@ -860,7 +874,7 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
 }
 
 // ---------------------------------------------------------------------------
-// Allocation-free backward (fa_bwd_noalloc): the [D | L log2(e)] workspace
+// Allocation-free backward (fa_bwd_noalloc): the [-D | L log2(e)] workspace
 // lives in this fixed device array, one copy per GPU, held until the process
 // ends.  Host code never passes the array's name to a kernel (on the host it
 // is only a stand-in): the device address of each GPU's copy is looked up

@@ -39,7 +39,7 @@ hipError_t launch_fwd_rows(const void* q, const void* k, const void* v, void* o,
 hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int H, int N, float scale, int causal, hipStream_t stream);
 
-// Backward workspace layout (2 B*H*N floats): [D = rowsum(dO * O) | L * log2(e)].
+// Backward workspace layout (2 B*H*N floats): [-D = -rowsum(dO * O) | L * log2(e)].
 hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* ws, int B, int H,
                           int N, hipStream_t stream);
 

@@ -85,7 +85,7 @@ int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* ls
 
 /*
  * Bytes of device workspace the backward pass needs for these sizes:
- * 2*B*H*N float32 (rounded up to 256 bytes), laid out as [D | L*log2(e)],
+ * 2*B*H*N float32 (rounded up to 256 bytes), laid out as [-D | L*log2(e)],
  * with D_i = sum_k dO_ik O_ik and L the forward's log-sum-exp.  Returns 0
  * when the sizes are invalid or empty.
  */
@@ -98,7 +98,7 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal);
  *   dq, dk, dv     : [B,H,N,d] bf16 outputs.
  *   workspace      : device buffer of at least fa_bwd_workspace_size() bytes,
  *                    16-byte aligned; its contents on entry are ignored and
- *                    on exit hold [D | L*log2(e)].
+ *                    on exit hold [-D | L*log2(e)].
  * P is recomputed tile by tile as exp(scale q.k - L_i); with
  * dP = dO V^T and D_i = sum_k dO_ik O_ik, dS = P o (dP - D), and
  * dV = P^T dO, dQ = scale dS K, dK = scale dS^T Q ("Interrogating the GPU,
@@ -116,7 +116,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, outputs, results
  * (bitwise those of fa_bwd) and error behaviour as fa_bwd, minus the
- * workspace.  It calls no allocator: the [D | L*log2(e)] workspace lives in a
+ * workspace.  It calls no allocator: the [-D | L*log2(e)] workspace lives in a
  * fixed array inside the library, FA_NOALLOC_SCRATCH_BYTES per GPU, which
  * each GPU the library runs on holds until the process ends.  Problems whose
  * workspace would not fit (B*H*N above FA_NOALLOC_MAX_ROWS) are rejected with
@@ -135,10 +135,12 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
  * caller can schedule or time them separately; running all three with the
  * same arguments and workspace is exactly fa_bwd.  Arguments as for fa_bwd.
  *
- * fa_bwd_preprocess: fills the workspace with D_i = sum_k dO_ik O_ik, the row
- *   sum of dO o O that plays the role of delta in dS = P o (dP - delta)
- *   ("Interrogating the GPU, part 5", section "What does the backward pass do
- *   without P?"), and with L_i log2(e) for the exp2-based recomputation.
+ * fa_bwd_preprocess: fills the workspace with -D_i = -sum_k dO_ik O_ik, D
+ *   being the row sum of dO o O that plays the role of delta in
+ *   dS = P o (dP - delta) ("Interrogating the GPU, part 5", section "What
+ *   does the backward pass do without P?"; stored negated because the other
+ *   two stages start their dP accumulations from it), and with L_i log2(e)
+ *   for the exp2-based recomputation.
  * fa_bwd_dkdv: for each key block, recompute P = exp(scale q.k - L) over all
  *   visible queries and accumulate dV = P^T dO and dK = scale dS^T Q.
  * fa_bwd_dq: for each query block, recompute P and dS over all visible keys

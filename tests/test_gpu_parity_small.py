@@ -136,3 +136,24 @@ def test_backward_small(fa, N, causal, BH):
     e = [max_err(from_dev(a), b) for a, b in ((dq, rdq), (dk, rdk), (dv, rdv))]
     print(f"bwd N={N} causal={causal} BH={BH}: dQ {e[0]:.2e} dK {e[1]:.2e} dV {e[2]:.2e}", flush=True)
     assert max(e) <= TOL_OUT
+
+
+@pytest.mark.parametrize("N", [1, 65, 300])
+def test_backward_workspace_contents(fa, N):
+    """After the backward the workspace holds what the header documents:
+    [-D | L log2(e)], D being the oracle's row sum of dO o O taken on the
+    kernel's own O, and L the forward's log-sum-exp."""
+    import torch
+    B, H = 2, 3
+    x = fa_inputs.make(B, H, N, seed=8500 + N, with_do=True)
+    q, k, v, do = (to_dev(x[n], torch) for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, fa_inputs.SCALE, True)
+    ws = fa.workspace_for(B, H, N, True, q.device)
+    fa.fa_bwd(q, k, v, o, do, lse, *(torch.empty_like(q) for _ in range(3)), fa_inputs.SCALE, True, ws)
+    torch.cuda.synchronize()
+    rows = B * H * N
+    w = ws[: 8 * rows].view(torch.float32).cpu().numpy().astype(np.float64)
+    D = ora.backward(f64(x["q"]), f64(x["k"]), f64(x["v"]), from_dev(o), f64(x["do"]),
+                     fa_inputs.SCALE, True)[3]
+    np.testing.assert_allclose(-w[:rows], D.reshape(-1), rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(w[rows:], from_dev(lse).reshape(-1) * math.log2(math.e), rtol=1e-6, atol=0)
