@@ -12,6 +12,13 @@ read or overwrite the destination registers of an inline-assembly MFMA, nor
 write its srcC registers, within MIN_WAIT wait states of it (an 8-pass 32x32
 MFMA needs about 11 for the first and fewer for the second).
 
+A second rule covers loads written as inline assembly: the compiler does not
+know such an instruction is a load whose data arrives later, so it inserts no
+wait before the destination registers are used, and it may copy them (a
+spill into AGPRs, say) the moment the statement ends.  A load into registers
+(as opposed to an LDS-direct load, which names no destination register) must
+therefore be an ordinary, compiler-visible load.
+
 Usage: python -m exact_io_aware_10_amd.asm_check FILE.s ...
 """
 from __future__ import annotations
@@ -63,11 +70,16 @@ def _written(op: str, ops: list) -> set:
 
 
 def check(text: str, min_wait: int = MIN_WAIT) -> list[str]:
-    """Return one message per early access to an inline-asm MFMA's result, or
-    early overwrite of its srcC registers."""
+    """Return one message per early access to an inline-asm MFMA's result,
+    early overwrite of its srcC registers, or inline-asm load into registers."""
     insts = _parse(text)
     problems = []
     for idx, (ln, op, ops, in_asm) in enumerate(insts):
+        if in_asm and op.startswith(("buffer_load", "global_load", "flat_load", "scratch_load",
+                                     "ds_read", "ds_load")) and _written(op, ops):
+            problems.append(f"line {ln}: {op} {' '.join(ops)} loads into registers from inline "
+                            f"assembly (the compiler cannot wait for it)")
+            continue
         if not (in_asm and op.startswith("v_mfma")):
             continue
         dst = _regs(ops[0])

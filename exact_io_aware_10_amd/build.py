@@ -52,7 +52,7 @@ def _check_asm(src: str) -> None:
     with open(asm) as f:
         problems = asm_check.check(f.read())
     if problems:
-        raise RuntimeError(f"{src}: inline-asm MFMA results read too early:\n" + "\n".join(problems))
+        raise RuntimeError(f"{src}: inline-assembly hazards:\n" + "\n".join(problems))
 
 
 MICRO_SRC = os.path.join(ROOT, "micro", "micro.hip")

@@ -570,8 +570,9 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   // Q^T and dO^T as B operands (zero past N): lane holds
   // Q[q0w + 32 g + col][16 kc + 8 h .. + 7].  Q is negated for a negative
   // scale and cleared for scale 0 (sl2 is |scale| log2 e; dQ = scale dS K
-  // takes the signed scale at the store), then moved to AGPRs.  dO is waited
-  // for below.
+  // takes the signed scale at the store), then moved to AGPRs.  Both are
+  // ordinary (compiler-tracked) loads, so that no copy of a fragment the
+  // register allocator makes can run ahead of the data.
   bf16x8 qf[2][8], df[2][8];
   u32x4 qraw[2][8];
 #pragma unroll
@@ -580,7 +581,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     for (int kc = 0; kc < 8; ++kc) {
       const uint32_t off = (uint32_t)(q0w + 32 * g + col) * kRowBytes + (2 * kc + h) * 16;
       qraw[g][kc] = buf_load16(rq, off);
-      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(df[g][kc]) : "v"(off), "s"(rdo) : "memory");
+      df[g][kc] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
     }
 #pragma unroll
   for (int g = 0; g < 2; ++g)

@@ -48,3 +48,13 @@ def test_reads_of_srcc_and_fenced_writes_are_accepted():
     assert asm_check.check(MFMA_C + "\ts_nop 15\n\tds_read_b128 v[40:43], v60\n") == []
     # An LDS-direct load names a VGPR as its address, not as a destination.
     assert asm_check.check(MFMA_C + "\tbuffer_load_dwordx4 v40, s[0:3], 0 offen lds\n") == []
+
+
+def test_inline_asm_load_into_registers_is_flagged():
+    # The compiler cannot wait for a load it does not know about (it copied
+    # such a destination into AGPRs before the data arrived once).
+    text = ";;#ASMSTART\n\tbuffer_load_dwordx4 v[4:7], v1, s[0:3], 0 offen\n;;#ASMEND\n"
+    assert len(asm_check.check(text)) == 1
+    # The same load emitted by the compiler, and an inline-asm LDS-direct load, pass.
+    assert asm_check.check("\tbuffer_load_dwordx4 v[4:7], v1, s[0:3], 0 offen\n") == []
+    assert asm_check.check(";;#ASMSTART\n\tbuffer_load_dwordx4 v1, s[0:3], 0 offen lds\n;;#ASMEND\n") == []
