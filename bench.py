@@ -11,7 +11,8 @@ device memory when the timed region starts.
 Prints ONE JSON line on stdout.  `value` is the step's credited TFLOP/s
 (forward 4 N^2 d B H, backward 2.5x that, both halved when causal); the
 per-kernel durations come from HIP events recorded on the launch stream
-around every kernel of every timed step.
+around every kernel of every timed step.  The board's power and graphics
+clock, sampled while the timed steps run, are reported under `power`.
 """
 from __future__ import annotations
 
@@ -22,6 +23,7 @@ import json
 import os
 import statistics
 import sys
+import threading
 import time
 
 
@@ -155,6 +157,105 @@ def gpu_clocks():
     return None
 
 
+class PowerSampler:
+    """Board power (hwmon power1_input, W) and graphics clock (the '*' level of
+    pp_dpm_sclk, MHz) of the first AMD GPU, sampled every 5 ms on a thread
+    while the timed steps run; summary() gives their mean, min and max and the
+    board's power cap (power1_cap).  Nothing is sampled where sysfs does not
+    expose them."""
+
+    def __init__(self, drm_root: str = "/sys/class/drm"):
+        self.card = self.power = self.cap = None
+        for card in sorted(glob.glob(os.path.join(drm_root, "card*", "device"))):
+            try:
+                if open(os.path.join(card, "vendor")).read().strip() != "0x1002":
+                    continue
+            except OSError:
+                continue
+            hw = sorted(glob.glob(os.path.join(card, "hwmon", "hwmon*", "power1_input")))
+            if hw:
+                self.card, self.power = card, hw[0]
+                cap = os.path.join(os.path.dirname(hw[0]), "power1_cap")
+                self.cap = cap if os.path.exists(cap) else None
+                break
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+
+    def _read(self):
+        w = int(open(self.power).read()) / 1e6
+        mhz = None
+        for line in open(os.path.join(self.card, "pp_dpm_sclk")):
+            if line.rstrip().endswith("*"):
+                mhz = float(line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
+        return w, mhz
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except (OSError, ValueError, IndexError):
+                return
+            self._stop.wait(0.005)
+
+    def start(self):
+        if self.power:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        if self._thread:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self, skip: float = 0.0):
+        """Statistics of the samples after the first `skip` fraction."""
+        kept = self.samples[int(len(self.samples) * skip):]
+        if not kept:
+            return None
+        watts = [w for w, _ in kept]
+        mhz = [m for _, m in kept if m is not None]
+        out = {"samples": len(watts), "interval_ms": 5, "power_w_mean": statistics.mean(watts),
+               "power_w_min": min(watts), "power_w_max": max(watts), "source": self.power}
+        if self.cap:
+            try:
+                out["power_cap_w"] = int(open(self.cap).read()) / 1e6
+            except (OSError, ValueError):
+                pass
+        if mhz:
+            out.update({"sclk_mhz_mean": statistics.mean(mhz), "sclk_mhz_min": min(mhz),
+                        "sclk_mhz_max": max(mhz)})
+        return out
+
+
+def hold_kernels(torch, fa, stream, seconds, kernels):
+    """Each kernel alone, back to back for `seconds`, with the board power and
+    clock sampled meanwhile; statistics over the second half of the samples
+    (the power reading has caught up with the load by then)."""
+    out = {}
+    for name, fn in kernels.items():
+        torch.cuda.synchronize()
+        time.sleep(0.5)  # let the board cool back towards idle between kernels
+        ps = PowerSampler()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ps.start()
+        n, t0 = 0, time.perf_counter()
+        ev[0].record(stream)
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(10):
+                fn()
+            n += 10
+            torch.cuda.synchronize()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ps.stop()
+        out[name] = {"ms": ev[0].elapsed_time(ev[1]) / n, "launches": n, **(ps.summary(skip=0.5) or {})}
+        log(f"hold {name}: {out[name]['ms']:.4f} ms, "
+            f"{out[name].get('power_w_mean', float('nan')):.0f} W, "
+            f"{out[name].get('sclk_mhz_mean', float('nan')):.0f} MHz")
+    return out
+
+
 def kernel_stats(samples):
     """mean, median and min of per-launch durations (ms)."""
     return {"mean": sum(samples) / len(samples), "median": statistics.median(samples),
@@ -238,6 +339,11 @@ def main():
                          "draws -- a diagnostic of how much the operands' switching activity "
                          "costs at the power cap (same instructions, same shapes); not the "
                          "metric's inputs, and the oracle baseline is skipped")
+    ap.add_argument("--hold", type=float, default=0.0, metavar="SECONDS",
+                    help="after the timed steps, run each kernel of the step alone, back to back, "
+                         "for SECONDS and report the board power and graphics clock while it "
+                         "runs (the power reading trails the load by a fraction of a second, so "
+                         "the timed steps alone are too short to show its steady state)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -321,6 +427,8 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
     clocks_before = gpu_clocks()
+    sampler = PowerSampler()
+    sampler.start()
 
     use_graph = args.graph == "on" or (args.graph == "auto" and not with_bwd and not flush_bytes)
     samples = {n: [] for n in names}
@@ -378,12 +486,18 @@ def main():
             samples[n] = [e[i].elapsed_time(e[i + 1]) for e in evs]
         ms_per_step = wall / args.steps * 1e3
         timing = "HIP events around every kernel; value from the host clock around the K steps"
+    sampler.stop()
     clocks_after = gpu_clocks()
+    power = sampler.summary()
     stats = {n: kernel_stats(v_) for n, v_ in samples.items()}
     kern_ms = {n: st["mean"] for n, st in stats.items()}
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step; per kernel mean/median/min (ms): "
         + ", ".join(f"{n} {t['mean']:.4f}/{t['median']:.4f}/{t['min']:.4f}" for n, t in stats.items()))
     log(f"clocks before {clocks_before}, after {clocks_after}")
+    if power:
+        log(f"board power over the timed steps: mean {power['power_w_mean']:.0f} W, max "
+            f"{power['power_w_max']:.0f} W (cap {power.get('power_cap_w', float('nan')):.0f} W), "
+            f"sclk mean {power.get('sclk_mhz_mean', float('nan')):.0f} MHz, {power['samples']} samples")
 
     peak = acc.MI355X_BF16_DENSE_TFLOPS
     fwd_f = acc.fwd_flops(B, H, N, d, causal)
@@ -406,6 +520,14 @@ def main():
     out_extra["kernel_ms_median"] = {n: st["median"] for n, st in stats.items()}
     out_extra["kernel_ms_min"] = {n: st["min"] for n, st in stats.items()}
     out_extra["clocks"] = {"before": clocks_before, "after": clocks_after}
+    out_extra["power"] = power
+
+    if args.hold > 0:
+        out_extra["power_per_kernel"] = hold_kernels(torch, fa, stream, args.hold, {
+            "fwd": lambda: fa.fa_fwd(q, k, v, o, lse, scale, causal, stream),
+            **({"bwd_dkdv": lambda: fa.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, scale, causal, stream),
+                "bwd_dq": lambda: fa.fa_bwd_dq(q, k, v, do, ws, dq, scale, causal, stream)}
+               if with_bwd else {})})
 
     # Roofline of the kernel that takes the most time per step.
     half = 0.5 if causal else 1.0

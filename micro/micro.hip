@@ -12,15 +12,31 @@
 //            one wave, interleaved.
 //   atomic   fp32 global atomic add bandwidth: every lane adds one float,
 //            rows of 256 bytes per wave, all to distinct addresses.
+//   mix1     one wave per SIMD issuing both streams: per MFMA, 0 to 4
+//            fma -> exp2 pairs interleaved (as a backward kernel's
+//            softmax rides on its MFMAs), accumulators in AGPRs (the
+//            compiler's choice) or in VGPRs (inline assembly, as the
+//            kernels keep S and dP); core cycles per MFMA.
+//   order    the same MFMA loop (random operands) for about a second per
+//            variant, with the order of the MFMAs changed so that
+//            consecutive MFMAs share none, one or both of their operand
+//            registers; the board's power (hwmon power1_input) and the
+//            graphics clock (pp_dpm_sclk) are sampled every 10 ms meanwhile.
 //
 // Every kernel writes only through vector stores, every access is to a
 // buffer sized on the host for exactly the grid launched, and every loop
 // has a fixed trip count.  Prints one JSON line per measurement.
 #include <hip/hip_runtime.h>
 
+#include <glob.h>
+
+#include <atomic>
+#include <chrono>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <string>
+#include <thread>
 #include <vector>
 
 #define CHECK(x)                                                                      \
@@ -61,6 +77,120 @@ __global__ __launch_bounds__(256) void mfma_rate(const u32x4* __restrict__ src, 
     for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[i ^ 1], c[i], 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i ^ 2], b[i ^ 3], c[i], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += c[i][j];
+  out[blockIdx.x * 256 + tid] = s;
+}
+
+// One wave per SIMD (one 256-thread block per CU), four accumulators (in
+// VGPRs when VACC); per MFMA, NPAIR fma -> exp2 pairs on independent values
+// in between.
+template <int NPAIR, int VACC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mix1(const u32x4* __restrict__ src, float* __restrict__ out, long long* __restrict__ cyc, int iters) {
+  const int tid = threadIdx.x;
+  bf16x8 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = __builtin_bit_cast(bf16x8, src[i * 256 + tid]);
+    b[i] = __builtin_bit_cast(bf16x8, src[(4 + i) * 256 + tid]);
+  }
+  f32x16 c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) c[i][j] = 0.f;
+  float f[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) f[j] = 0.001f * tid + 0.01f * j - 0.5f;
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (VACC)
+        asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                     : "+v"(c[i & 3])
+                     : "v"(a[i & 3]), "v"(b[(i + 1) & 3]));
+      else
+        c[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i & 3], b[(i + 1) & 3], c[i & 3], 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NPAIR; ++j) {
+        const int k = (4 * i + j) & 31;
+        f[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(f[k], 0.5f, -0.25f));
+        asm volatile("" : "+v"(f[k]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // the VGPR results are read by VALU only after the last MFMA has drained
+  if (VACC) asm volatile("s_nop 15\n\ts_nop 15" : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]));
+  const long long t1 = __builtin_amdgcn_s_memtime();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += c[i][j];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) s += f[j];
+  out[blockIdx.x * 256 + tid] = s;
+  if ((tid & 63) == 0) cyc[blockIdx.x * 4 + (tid >> 6)] = t1 - t0;
+}
+
+// The same loop with the MFMAs in a fixed order (sched_barrier between them):
+//   0  consecutive MFMAs share no operand register
+//   1  the A operand is held for two MFMAs, B changes every MFMA
+//   2  A held for four MFMAs
+//   3  B held for four MFMAs, A changes every MFMA
+//   4  A and B both held for four MFMAs (four accumulators)
+template <int ORDER>
+__device__ __forceinline__ void order_ops(int n, int i, int& ai, int& bi) {
+  // n: half of the iteration (0, 1); i: MFMA within the half (0..3)
+  if (ORDER == 0) {
+    ai = n ? (i ^ 2) : i;
+    bi = n ? (i ^ 3) : (i ^ 1);
+  } else if (ORDER == 1) {
+    ai = 2 * n + (i >> 1);
+    bi = i;
+  } else if (ORDER == 2) {
+    ai = n;
+    bi = i;
+  } else if (ORDER == 3) {
+    ai = i;
+    bi = n;
+  } else {
+    ai = n;
+    bi = n;
+  }
+}
+template <int ORDER>
+__global__ __launch_bounds__(256) void mfma_order(const u32x4* __restrict__ src, float* __restrict__ out,
+                                                  int iters) {
+  const int tid = threadIdx.x;
+  bf16x8 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = __builtin_bit_cast(bf16x8, src[i * 256 + tid]);
+    b[i] = __builtin_bit_cast(bf16x8, src[(4 + i) * 256 + tid]);
+  }
+  f32x16 c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) c[i][j] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int ai, bi;
+        order_ops<ORDER>(n, i, ai, bi);
+        c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ai], b[bi], c[i], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
   }
   float s = 0.f;
 #pragma unroll
@@ -241,6 +371,42 @@ static unsigned lcg(unsigned& s) {
   return s;
 }
 
+// Board power (W) and graphics clock (MHz) of the first AMD GPU, from sysfs;
+// negative when not readable.
+struct telemetry {
+  std::string power_path, sclk_path;
+  telemetry() {
+    glob_t g;
+    if (glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input", 0, nullptr, &g) == 0 && g.gl_pathc)
+      power_path = g.gl_pathv[0];
+    globfree(&g);
+    if (glob("/sys/class/drm/card*/device/pp_dpm_sclk", 0, nullptr, &g) == 0 && g.gl_pathc)
+      sclk_path = g.gl_pathv[0];
+    globfree(&g);
+  }
+  double power_w() const {
+    FILE* f = fopen(power_path.c_str(), "r");
+    if (!f) return -1;
+    double uw = -1;
+    if (fscanf(f, "%lf", &uw) != 1) uw = -1;
+    fclose(f);
+    return uw < 0 ? -1 : uw / 1e6;
+  }
+  double sclk_mhz() const {  // the DPM level marked '*'
+    FILE* f = fopen(sclk_path.c_str(), "r");
+    if (!f) return -1;
+    char line[128];
+    double mhz = -1;
+    while (fgets(line, sizeof line, f)) {
+      if (!strchr(line, '*')) continue;
+      const char* c = strchr(line, ':');
+      if (c) mhz = atof(c + 1);
+    }
+    fclose(f);
+    return mhz;
+  }
+};
+
 static float time_ms(hipEvent_t e0, hipEvent_t e1) {
   float ms = 0.f;
   CHECK(hipEventElapsedTime(&ms, e0, e1));
@@ -290,6 +456,83 @@ int main(int argc, char** argv) {
           printf("{\"probe\": \"mfma_bf16_32x32x16\", \"operands\": \"%s\", \"ms\": %.3f, \"tflops\": %.1f}\n",
                  rnd_ops ? "random" : "constant", ms, flop / ms / 1e9);
       }
+    }
+  }
+  if (!*only || !strcmp(only, "mix1")) {
+    CHECK(hipMemcpy(src, rnd.data(), nfrag * 16, hipMemcpyHostToDevice));
+    const int iters = 2000, grid = kCUs;  // one block of four waves per CU: one wave per SIMD
+    for (int v = 0; v < 2; ++v)
+    for (int np = 0; np <= 4; ++np) {
+      for (int w = 0; w < 2; ++w) {
+        switch (np + 5 * v) {
+          case 0: hipLaunchKernelGGL((mix1<0, 0>), dim3(grid), dim3(256), 0, 0, src, out, cyc, iters); break;
+          case 1: hipLaunchKernelGGL((mix1<1, 0>), dim3(grid), dim3(256), 0, 0, src, out, cyc, iters); break;
+          case 2: hipLaunchKernelGGL((mix1<2, 0>), dim3(grid), dim3(256), 0, 0, src, out, cyc, iters); break;
+          case 3: hipLaunchKernelGGL((mix1<3, 0>), dim3(grid), dim3(256), 0, 0, src, out, cyc, iters); break;
+          case 4: hipLaunchKernelGGL((mix1<4, 0>), dim3(grid), dim3(256), 0, 0, src, out, cyc, iters); break;
+          case 5: hipLaunchKernelGGL((mix1<0, 1>), dim3(grid), dim3(256), 0, 0, src, out, cyc, iters); break;
+          case 6: hipLaunchKernelGGL((mix1<1, 1>), dim3(grid), dim3(256), 0, 0, src, out, cyc, iters); break;
+          case 7: hipLaunchKernelGGL((mix1<2, 1>), dim3(grid), dim3(256), 0, 0, src, out, cyc, iters); break;
+          case 8: hipLaunchKernelGGL((mix1<3, 1>), dim3(grid), dim3(256), 0, 0, src, out, cyc, iters); break;
+          default: hipLaunchKernelGGL((mix1<4, 1>), dim3(grid), dim3(256), 0, 0, src, out, cyc, iters); break;
+        }
+        CHECK(hipDeviceSynchronize());
+      }
+      CHECK(hipMemcpy(hc.data(), cyc, (size_t)grid * 4 * sizeof(long long), hipMemcpyDeviceToHost));
+      double avg = 0;
+      for (int i = 0; i < grid * 4; ++i) avg += (double)hc[i];
+      avg /= grid * 4;
+      printf("{\"probe\": \"mix1\", \"accumulators\": \"%s\", \"fma_exp_pairs_per_mfma\": %d, "
+             "\"core_cycles_per_mfma\": %.1f}\n", v ? "VGPR" : "AGPR", np, avg / (iters * 8.0));
+    }
+  }
+  if (!*only || !strcmp(only, "order")) {
+    CHECK(hipMemcpy(src, rnd.data(), nfrag * 16, hipMemcpyHostToDevice));
+    const telemetry tel;
+    const char* names[5] = {"no operand shared", "A held for 2", "A held for 4", "B held for 4",
+                            "A and B held for 4"};
+    const int grid = 2 * kCUs, iters = 20000, launches = 160;  // about a second per variant
+    for (int order = 0; order < 5; ++order) {
+      auto launch = [&](int it) {
+        switch (order) {
+          case 0: hipLaunchKernelGGL(mfma_order<0>, dim3(grid), dim3(256), 0, 0, src, out, it); break;
+          case 1: hipLaunchKernelGGL(mfma_order<1>, dim3(grid), dim3(256), 0, 0, src, out, it); break;
+          case 2: hipLaunchKernelGGL(mfma_order<2>, dim3(grid), dim3(256), 0, 0, src, out, it); break;
+          case 3: hipLaunchKernelGGL(mfma_order<3>, dim3(grid), dim3(256), 0, 0, src, out, it); break;
+          default: hipLaunchKernelGGL(mfma_order<4>, dim3(grid), dim3(256), 0, 0, src, out, it); break;
+        }
+      };
+      launch(100);
+      CHECK(hipDeviceSynchronize());
+      std::this_thread::sleep_for(std::chrono::milliseconds(500));
+      std::atomic<bool> stop{false};
+      std::vector<double> pw, sc;
+      std::thread sampler([&] {
+        while (!stop.load()) {
+          pw.push_back(tel.power_w());
+          sc.push_back(tel.sclk_mhz());
+          std::this_thread::sleep_for(std::chrono::milliseconds(10));
+        }
+      });
+      CHECK(hipEventRecord(e0));
+      for (int l = 0; l < launches; ++l) launch(iters);
+      CHECK(hipEventRecord(e1));
+      CHECK(hipDeviceSynchronize());
+      stop = true;
+      sampler.join();
+      const double ms = time_ms(e0, e1);
+      const double flop = (double)launches * grid * 4 * iters * 8 * 32.0 * 32 * 16 * 2;
+      // mean over the second half of the samples (past the clock's settling)
+      double p = 0, c = 0;
+      size_t n0 = pw.size() / 2, n = 0;
+      for (size_t i = n0; i < pw.size(); ++i, ++n) {
+        p += pw[i];
+        c += sc[i];
+      }
+      printf("{\"probe\": \"mfma_order\", \"order\": \"%s\", \"ms\": %.1f, \"tflops\": %.1f, "
+             "\"power_w\": %.1f, \"sclk_mhz\": %.0f, \"samples\": %zu}\n",
+             names[order], ms, flop / ms / 1e9, n ? p / n : -1.0, n ? c / n : -1.0, n);
+      fflush(stdout);
     }
   }
   if (!*only || !strcmp(only, "valu")) {
