@@ -97,9 +97,14 @@ def cpu_model() -> str:
     return "unknown"
 
 
+CPU_MIN_SECONDS = 10.0  # the sample is repeated until the oracle has run this long
+
+
 def cpu_baseline(x, w, heads: int):
     """The fp64 oracle (forward, and backward where the workload has one) on
-    heads 0 .. heads-1 of batch 0, after an untimed warm-up on a small head."""
+    heads 0 .. heads-1 of batch 0, after an untimed warm-up on a small head;
+    the sample is run again until CPU_MIN_SECONDS have passed (small
+    workloads), and the rate is the credited FLOPs over the total time."""
     from oracle import attention as ora
     from threadpoolctl import threadpool_info
     blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
@@ -113,23 +118,28 @@ def cpu_baseline(x, w, heads: int):
         ora.backward(WQ, WK, WV, wo, WD, fa_inputs.SCALE, w["causal"])
     sl = (slice(0, 1), slice(0, heads))
     Q, K, V = (fa_inputs.bf16_bits_to_f64(x[n][sl]) for n in "qkv")
-    t0 = time.perf_counter()
-    o, _ = ora.forward(Q, K, V, fa_inputs.SCALE, w["causal"])
+    DO = fa_inputs.bf16_bits_to_f64(x["do"][sl]) if has_bwd else None
     flops = acc.fwd_flops(1, heads, w["N"], 128, w["causal"])
     if has_bwd:
-        DO = fa_inputs.bf16_bits_to_f64(x["do"][sl])
-        ora.backward(Q, K, V, o, DO, fa_inputs.SCALE, w["causal"])
         flops += acc.bwd_flops(1, heads, w["N"], 128, w["causal"])
-    dt = time.perf_counter() - t0
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < CPU_MIN_SECONDS:
+        t0 = time.perf_counter()
+        o, _ = ora.forward(Q, K, V, fa_inputs.SCALE, w["causal"])
+        if has_bwd:
+            ora.backward(Q, K, V, o, DO, fa_inputs.SCALE, w["causal"])
+        dt += time.perf_counter() - t0
+        reps += 1
     return {
-        "value": flops / dt / 1e12,
+        "value": flops * reps / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": ORACLE_THREADS,
         "kind": "oracle",
         "sample": (f"fp64 oracle {'forward+backward' if has_bwd else 'forward'} on heads 0-{heads - 1} "
-                   f"of batch 0 of the same workload, {dt:.1f} s wall after a warm-up on 256 rows; "
-                   f"credited FLOPs of that sample"),
+                   f"of batch 0 of the same workload, run {reps} time(s), {dt:.1f} s wall in all "
+                   f"after a warm-up on 256 rows; credited FLOPs of that sample"),
         "seconds": dt,
+        "repetitions": reps,
         "blas_threads": max(blas, default=None),
         "affinity_cores": len(os.sched_getaffinity(0)),
         "host_cpu": cpu_model(),
