@@ -17,6 +17,16 @@
 //            softmax rides on its MFMAs), accumulators in AGPRs (the
 //            compiler's choice) or in VGPRs (inline assembly, as the
 //            kernels keep S and dP); core cycles per MFMA.
+//   lds      LDS read bandwidth per CU for ds_read_b128, ds_read_b64 and
+//            ds_read_b64_tr_b16 (eight waves per CU, consecutive lanes on
+//            consecutive addresses: no bank conflicts); core cycles from
+//            s_memtime.
+//   copy     HBM bandwidth of a plain 1 GiB device copy (16-byte loads and
+//            stores, grid-stride).
+//   atomicdq the atomic traffic a dK/dV kernel with fused fp32 dQ would issue
+//            at B1 H64 N8192 causal: per head and 256-key block, one
+//            32 x 128 fp32 add per 32-query tile at or after the block;
+//            the result (a count per dQ element) is checked on the host.
 //   order    the same MFMA loop (random operands) for about a second per
 //            variant, with the order of the MFMAs changed so that
 //            consecutive MFMAs share none, one or both of their operand
@@ -51,6 +61,9 @@
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kCUs = 256;
 
@@ -366,6 +379,79 @@ __global__ __launch_bounds__(256) void atomic_rate(float* __restrict__ dst, int 
 }
 
 // ---------------------------------------------------------------------------
+// LDS read bandwidth: 512 threads (eight waves) per block, one block per CU
+// (96 KiB of LDS per block: a second block does not fit beside it), a 64 KiB
+// LDS array read in a loop, eight reads per iteration, each a wave-wide
+// contiguous span; the base offset moves every iteration through a register
+// the compiler cannot follow, so no read can be hoisted out of the loop.
+// KIND 0: ds_read_b128, 1: ds_read_b64, 2: ds_read_b64_tr_b16.  cyc gets
+// each wave's s_memtime cycles.
+constexpr int kLdsWords = 16384;  // 64 KiB of u32
+template <int KIND>
+__global__ __launch_bounds__(512) void lds_rate(unsigned* __restrict__ out, long long* __restrict__ cyc,
+                                                int iters) {
+  __shared__ __attribute__((aligned(16))) unsigned buf[kLdsWords];
+  __shared__ unsigned pad[kLdsWords / 2];  // only occupies LDS
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kLdsWords; i += 512) buf[i] = (unsigned)i * 2654435761u;
+  __syncthreads();
+  const char* base = reinterpret_cast<const char*>(buf);
+  constexpr int kBytes = KIND == 0 ? 16 : 8;  // per lane and read
+  constexpr int kSpan = 64 * kBytes;          // per wave and read
+  constexpr int kMask = kLdsWords * 4 - 1;
+  unsigned x = 0;
+  int b = wave * kSpan + lane * kBytes;
+  const long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      // wave-wide span u of this iteration, wrapped inside the 64 KiB array
+      const int off = (b + u * 8 * kSpan) & kMask;
+      if (KIND == 0) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(base + off);
+        x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+      } else if (KIND == 1) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(base + off);
+        x ^= v[0] ^ v[1];
+      } else {
+        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off));
+        x ^= (unsigned)(unsigned short)v[0] ^ (unsigned)(unsigned short)v[3];
+      }
+    }
+    b = (b + 3 * kSpan) & kMask;
+    asm volatile("" : "+v"(b));
+  }
+  const long long t1 = __builtin_amdgcn_s_memtime();
+  pad[tid] = x;
+  out[blockIdx.x * 512 + tid] = x ^ pad[tid ^ 1];
+  if (lane == 0) cyc[blockIdx.x * 8 + wave] = t1 - t0;
+}
+
+// Plain copy, 16 bytes per lane per iteration, grid-stride.
+__global__ __launch_bounds__(256) void copy16(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                              long long n) {
+  const long long stride = (long long)gridDim.x * 256;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+// The fused-dQ atomic traffic: block (head, key block kb of 256 keys) adds
+// 1.0 to every element of the 32 x 128 dQ rows of each 32-query tile
+// qt = 8 kb .. N / 32 - 1 (the tiles at or after the block, causal).
+// dq holds heads x n rows x 128 floats.
+__global__ __launch_bounds__(256) void atomic_dq(float* __restrict__ dq, int n) {
+  const int nkb = n / 256;
+  const int head = blockIdx.x / nkb, kb = blockIdx.x % nkb;
+  float* hq = dq + (size_t)head * n * 128;
+  for (int qt = 8 * kb; qt < n / 32; ++qt) {
+    float* tile = hq + (size_t)qt * 32 * 128;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      __hip_atomic_fetch_add(tile + j * 256 + threadIdx.x, 1.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ---------------------------------------------------------------------------
 static unsigned lcg(unsigned& s) {
   s = s * 1664525u + 1013904223u;
   return s;
@@ -625,6 +711,88 @@ int main(int argc, char** argv) {
     const double bytes = (double)threads * iters * 4;
     printf("{\"probe\": \"atomic_add_f32\", \"ms\": %.3f, \"gbps\": %.1f}\n", ms, bytes / ms / 1e6);
     CHECK(hipFree(dst));
+  }
+  if (!*only || !strcmp(only, "lds")) {
+    const int grid = kCUs, iters = 4096;
+    unsigned* lout;
+    long long* lcyc;
+    CHECK(hipMalloc(&lout, (size_t)grid * 512 * sizeof(unsigned)));
+    CHECK(hipMalloc(&lcyc, (size_t)grid * 8 * sizeof(long long)));
+    std::vector<long long> hl((size_t)grid * 8);
+    const char* names[3] = {"ds_read_b128", "ds_read_b64", "ds_read_b64_tr_b16"};
+    const int bytes[3] = {16, 8, 8};
+    for (int kind = 0; kind < 3; ++kind) {
+      for (int w = 0; w < 2; ++w) {
+        if (kind == 0)
+          hipLaunchKernelGGL(lds_rate<0>, dim3(grid), dim3(512), 0, 0, lout, lcyc, iters);
+        else if (kind == 1)
+          hipLaunchKernelGGL(lds_rate<1>, dim3(grid), dim3(512), 0, 0, lout, lcyc, iters);
+        else
+          hipLaunchKernelGGL(lds_rate<2>, dim3(grid), dim3(512), 0, 0, lout, lcyc, iters);
+        CHECK(hipDeviceSynchronize());
+      }
+      CHECK(hipMemcpy(hl.data(), lcyc, hl.size() * sizeof(long long), hipMemcpyDeviceToHost));
+      double avg = 0;
+      for (long long c : hl) avg += (double)c;
+      avg /= (double)hl.size();
+      const double per_cu = 8.0 * iters * 8 * 64 * bytes[kind];  // eight waves per CU
+      printf("{\"probe\": \"lds_read\", \"instruction\": \"%s\", \"bytes_per_core_cycle_per_cu\": %.1f}\n",
+             names[kind], per_cu / avg);
+    }
+    CHECK(hipFree(lout));
+    CHECK(hipFree(lcyc));
+  }
+  if (!*only || !strcmp(only, "copy")) {
+    const long long n = (1LL << 30) / 16;  // 1 GiB
+    u32x4 *a, *b;
+    CHECK(hipMalloc(&a, n * 16));
+    CHECK(hipMalloc(&b, n * 16));
+    CHECK(hipMemset(a, 1, n * 16));
+    const int grid = 8 * kCUs;
+    hipLaunchKernelGGL(copy16, dim3(grid), dim3(256), 0, 0, a, b, n);
+    CHECK(hipDeviceSynchronize());
+    const int reps = 10;
+    CHECK(hipEventRecord(e0));
+    for (int r = 0; r < reps; ++r) hipLaunchKernelGGL(copy16, dim3(grid), dim3(256), 0, 0, a, b, n);
+    CHECK(hipEventRecord(e1));
+    CHECK(hipDeviceSynchronize());
+    const double ms = time_ms(e0, e1) / reps;
+    printf("{\"probe\": \"hbm_copy\", \"bytes_copied\": %lld, \"ms\": %.3f, \"gbps_read_plus_write\": %.0f}\n",
+           n * 16, ms, 2.0 * n * 16 / ms / 1e6);
+    CHECK(hipFree(a));
+    CHECK(hipFree(b));
+  }
+  if (!*only || !strcmp(only, "atomicdq")) {
+    const int heads = 64, n = 8192;
+    const size_t elems = (size_t)heads * n * 128;  // 256 MiB of fp32
+    float* dq;
+    CHECK(hipMalloc(&dq, elems * sizeof(float)));
+    const int grid = heads * (n / 256);
+    double ms = 0;
+    for (int r = 0; r < 2; ++r) {  // the second, timed launch starts from zero too
+      CHECK(hipMemset(dq, 0, elems * sizeof(float)));
+      CHECK(hipDeviceSynchronize());
+      CHECK(hipEventRecord(e0));
+      hipLaunchKernelGGL(atomic_dq, dim3(grid), dim3(256), 0, 0, dq, n);
+      CHECK(hipEventRecord(e1));
+      CHECK(hipDeviceSynchronize());
+      ms = time_ms(e0, e1);
+    }
+    // Every element of query row q was added once per key block kb <= q / 256.
+    std::vector<float> row(128);
+    bool ok = true;
+    for (int q : {0, 255, 256, 4095, 8191}) {
+      for (int hh : {0, 63}) {
+        CHECK(hipMemcpy(row.data(), dq + ((size_t)hh * n + q) * 128, 128 * sizeof(float), hipMemcpyDeviceToHost));
+        for (float v : row) ok = ok && v == (float)(q / 256 + 1);
+      }
+    }
+    double adds = 0;
+    for (int kb = 0; kb < n / 256; ++kb) adds += (double)(n / 32 - 8 * kb) * 32 * 128;
+    adds *= heads;
+    printf("{\"probe\": \"atomic_dq_b1_h64_n8192_causal\", \"atomic_bytes\": %.0f, \"ms\": %.3f, "
+           "\"gbps\": %.0f, \"result_checked\": %s}\n", adds * 4, ms, adds * 4 / ms / 1e6, ok ? "true" : "false");
+    CHECK(hipFree(dq));
   }
   CHECK(hipFree(src));
   CHECK(hipFree(out));
