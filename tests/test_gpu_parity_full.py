@@ -189,3 +189,35 @@ def test_fwd_bwd_causal_b2_h16_n4096_every_head(fa):
 def test_fwd_bwd_causal_b1_h64_n8192_every_head(fa):
     """The benchmark's workload: O, LSE, dQ, dK, dV on all 64 heads."""
     _backward_every_head(fa, "causal_b1_h64_n8192")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("scale", [-fa_inputs.SCALE, 0.0])
+def test_fwd_bwd_other_scales_b2_h16_n4096(fa, scale):
+    """A negative scale (the kernels fold its sign into the operand they hold
+    in registers) and scale 0 (uniform attention over the visible keys) at a
+    full workload size, causal, through the benchmark's launch configuration:
+    O, LSE, dQ, dK, dV of two whole heads against the oracle."""
+    import torch
+    x = fa_inputs.make_workload("causal_b2_h16_n4096", with_do=True)
+    q, k, v, do = (to_dev(x[n], torch) for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, scale, True)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, scale, True)
+    torch.cuda.synchronize()
+    O, L = from_dev(o), from_dev(lse)
+    G = [from_dev(t) for t in (dq, dk, dv)]
+    for t in [O, L] + G:
+        assert np.isfinite(t).all()
+
+    def one(bh):
+        b, hh = bh
+        sl = (slice(b, b + 1), slice(hh, hh + 1))
+        Q, K, V, DO = (f64(x[n][sl]) for n in ("q", "k", "v", "do"))
+        ro, rl = ora.forward(Q, K, V, scale, True)
+        rdq, rdk, rdv, _ = ora.backward(Q, K, V, ro, DO, scale, True)
+        return (max_err(O[sl], ro), max_err(L[sl], rl)) + tuple(
+            max_err(g[sl], r) for g, r in zip(G, (rdq, rdk, rdv)))
+
+    errs = np.array(map_heads(one, [(0, 0), (1, 15)], f"scale {scale}", workers=2))
+    report(f"B2 H16 N4096 causal, scale {scale:+.4f}, heads (0, 0) and (1, 15)",
+           dict(zip(("O", "LSE", "dQ", "dK", "dV"), errs.max(axis=0))))
