@@ -1,11 +1,14 @@
 // Forward kernel: exact softmax attention by tiling with an online softmax.
 //
-// One workgroup owns FWD_BR = 128 query rows of one (batch, head) and streams
+// One workgroup owns FWD_BR = 256 query rows of one (batch, head) and streams
 // the head's keys and values through LDS in tiles of FWD_BC = 64 rows; each
-// of its 4 wavefronts owns 32 of the query rows ("Interrogating the GPU,
-// part 5: FlashAttention", sections "How does tiling remove the traffic?" and
-// "What did FlashAttention-2 fix?": queries split across warps, outer loop
-// over query blocks, grid over query blocks x heads).
+// of its 8 wavefronts (two per SIMD) owns 32 of the query rows
+// ("Interrogating the GPU, part 5: FlashAttention", sections "How does tiling
+// remove the traffic?" and "What did FlashAttention-2 fix?": queries split
+// across warps, outer loop over query blocks, grid over query blocks x
+// heads).  Each K/V tile brought into LDS serves 256 queries: half the L2 and
+// fabric traffic of 128-row blocks, which at the board's power cap is worth
+// more than the freedom of two independent workgroups per CU.
 //
 // Per tile and wave:
 //   S^T = K_j Q_i^T         bf16 MFMA 32x32x16, fp32 accumulate (C: key rows,
@@ -28,13 +31,15 @@
 
 namespace fa {
 
-constexpr int FWD_BR = 128;
-constexpr int FWD_WAVES = 4;
+constexpr int FWD_BR = 256;
+constexpr int FWD_WAVES = 8;
 constexpr int FWD_QW = FWD_BR / FWD_WAVES;  // 32 query rows per wave
 constexpr int FWD_BC = 64;
 constexpr int FWD_TILE = FWD_BC * kRowBytes;  // 16 KiB per K or V tile
 constexpr int FWD_THREADS = FWD_WAVES * 64;
 constexpr int FWD_LOADS = FWD_TILE / 1024 / FWD_WAVES;  // 1 KiB LDS-direct loads per wave
+static_assert(FWD_QW == 32 && 4 * FWD_WAVES * FWD_LOADS == FWD_BC,
+              "the tile loader's rows 4 FWD_WAVES n + 4 w + lane / 16 cover one tile exactly");
 
 // Rows whose running maximum grows by less than this (log2 units) keep the
 // stale maximum: P is then bounded by 2^kTau and the O / l rescale is skipped
@@ -89,14 +94,14 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int ntiles = (kend + FWD_BC - 1) / FWD_BC;
 
   // Tile loader: LDS-direct buffer loads.  Instruction n of wave w fills rows
-  // 16 n + 4 w .. + 3 (1 KiB, lane-linear in LDS); lane i lands on physical
+  // 32 n + 4 w .. + 3 (1 KiB, lane-linear in LDS); lane i lands on physical
   // chunk i % 16 of its row and so fetches the logical chunk stored there.
   // The tile's row offset is added to the per-lane offset, the part the
   // hardware range-checks, so rows past N read as zero.
   uint32_t ld_voff[FWD_LOADS];
 #pragma unroll
   for (int n = 0; n < FWD_LOADS; ++n) {
-    const int row = 16 * n + 4 * wave + (lane >> 4);
+    const int row = 4 * FWD_WAVES * n + 4 * wave + (lane >> 4);
     ld_voff[n] = (uint32_t)row * kRowBytes + (((lane & 15) ^ swz(row)) << 4);
   }
   auto issue_tile = [&](int t, auto bufc) {
@@ -105,7 +110,7 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint32_t toff = (uint32_t)t * FWD_TILE;
 #pragma unroll
     for (int n = 0; n < FWD_LOADS; ++n) {
-      const int row0 = 16 * n + 4 * wave;
+      const int row0 = 4 * FWD_WAVES * n + 4 * wave;
       buf_load16_lds(rk, kb + row0 * kRowBytes, ld_voff[n] + toff);
       buf_load16_lds(rv, vb + row0 * kRowBytes, ld_voff[n] + toff);
     }
@@ -515,10 +520,11 @@ void fwd_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   }
 }
 
-// Below these row-block grid sizes the key-split kernel runs (measured on
-// small shapes: it is 1.5-1.9x faster up to 64 row-block workgroups, and up to
-// 128 when causal, where the row blocks also differ in length; from 128
-// non-causal or 256 causal workgroups the row-block kernel is faster).
+// Below these grid sizes (in 256-row blocks) the key-split kernel runs.
+// Measured on B1 with N from 1024 to 8192: non-causal, the key split is
+// faster up to 64 row blocks (by 1.3-2.5x) and the row kernel from 128 (by
+// 1.3x); causal, where the row blocks also differ in length, the key split is
+// faster up to 128 row blocks and the row kernel from 256.
 constexpr int kSplitBelow = 128;
 constexpr int kSplitBelowCausal = 256;
 
