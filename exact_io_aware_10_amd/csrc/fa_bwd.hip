@@ -389,11 +389,13 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     // one element per MFMA; sched_barrier keeps the compiler to that order.
     const float* lb = reinterpret_cast<const float*>(smem + lsl);
     const int pq = psl * KV_SLOT, po = pq + KV_TILE;
-    bf16x8 npb[2][2], nsb[2][2];
     bf16x8 a_do[2], a_q[2];
     f32x4 l4[2];
+    // Product step n covers query half u = n / 4 of the previous tile and
+    // output block mb = n % 4, so that the packed P and dS of half u are last
+    // read at step 4 u + 3 and this tile's can take their registers there.
     auto rdt = [&](int n, int b) {
-      const int mb = n >> 1, ro2 = 16 * (n & 1) * kRowBytes;
+      const int mb = n & 3, ro2 = 16 * (n >> 2) * kRowBytes;
       a_do[b] = join(lds_read_tr(smem + po + ro2 + tro[mb][0]), lds_read_tr(smem + po + ro2 + tro[mb][1]));
       a_q[b] = join(lds_read_tr(smem + pq + ro2 + tro[mb][0]), lds_read_tr(smem + pq + ro2 + tro[mb][1]));
     };
@@ -406,7 +408,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      const int b = n & 1, mb = n >> 1, u = n & 1;
+      const int b = n & 1, mb = n & 3, u = n >> 2;
       const int gg = n >> 1, g = n & 1;
       if (n < 7) rdt(n + 1, b ^ 1);
       if (g == 1 && gg < 3) rdl(gg + 1);
@@ -424,22 +426,20 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         dp[g][i] = p * dp[g][i];  // dp holds dP - D
         __builtin_amdgcn_sched_barrier(0);
       }
-      // Rows 8 v .. 8 v + 7 of key group g are done after row group 2 v + 1.
-      if (gg & 1) {
-        const int v = gg >> 1, e = 8 * v;
-        npb[g][v] = pack8(s[g][e], s[g][e + 1], s[g][e + 2], s[g][e + 3], s[g][e + 4], s[g][e + 5],
-                          s[g][e + 6], s[g][e + 7]);
-        nsb[g][v] = pack8(dp[g][e], dp[g][e + 1], dp[g][e + 2], dp[g][e + 3], dp[g][e + 4],
-                          dp[g][e + 5], dp[g][e + 6], dp[g][e + 7]);
+      // Rows 8 v .. 8 v + 7 (row groups 2 v, 2 v + 1) of both key groups are
+      // done after step 4 v + 3, the last that reads the previous tile's half
+      // v: pack this tile's into those registers.
+      if ((n & 3) == 3) {
+        const int v = n >> 2, e = 8 * v;
+#pragma unroll
+        for (int gk = 0; gk < 2; ++gk) {
+          pb[gk][v] = pack8(s[gk][e], s[gk][e + 1], s[gk][e + 2], s[gk][e + 3], s[gk][e + 4],
+                            s[gk][e + 5], s[gk][e + 6], s[gk][e + 7]);
+          sb[gk][v] = pack8(dp[gk][e], dp[gk][e + 1], dp[gk][e + 2], dp[gk][e + 3], dp[gk][e + 4],
+                            dp[gk][e + 5], dp[gk][e + 6], dp[gk][e + 7]);
+        }
       }
     }
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        pb[g][u] = npb[g][u];
-        sb[g][u] = nsb[g][u];
-      }
   };
 
   // Slot 3 feeds the first step's dV / dK products: clear it.
