@@ -713,11 +713,13 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     acc_fence8(acc);
   };
 
-  // Step t (slot SL = t % 4): phases A, B, C as described above; the dQ
-  // products of phase C belong to tile t - 1 (zero dS before the first tile).
-  auto step = [&](int t) {
-    const int SL = t & (DQ_NSLOT - 1);
-    const int PSL = (t - 1) & (DQ_NSLOT - 1);
+  // Step t (slot SL = t % 4, a compile-time constant so that every LDS
+  // offset into the slot folds into the instructions): phases A, B, C as
+  // described above; the dQ products of phase C belong to tile t - 1 (zero dS
+  // before the first tile).
+  auto step = [&](int t, auto slc) {
+    constexpr int SL = decltype(slc)::value;
+    constexpr int PSL = (SL + DQ_NSLOT - 1) % DQ_NSLOT;
     // Tile t has landed once only tile t + 1's loads may be in flight; the
     // barrier publishes it and frees the slot of tile t - 2, which tile t + 2
     // takes (tile t - 1 is still read here, in phase C).
@@ -803,7 +805,12 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   }
   issue_tile(0, 0);
   issue_tile(1, 1);
-  for (int t = 0; t < tw; ++t) step(t);
+  for (int t = 0; t < tw; t += 4) {
+    step(t, kv_ic<0>{});
+    if (t + 1 < tw) step(t + 1, kv_ic<1>{});
+    if (t + 2 < tw) step(t + 2, kv_ic<2>{});
+    if (t + 3 < tw) step(t + 3, kv_ic<3>{});
+  }
   // Step tw: the last tile's dQ products; then the wave only keeps the ring
   // going up to the workgroup's step nt.
   for (int tt = tw; tt <= nt; ++tt) {
