@@ -2,7 +2,7 @@
 """Throughput of the exact-attention hot path on one MI355X.
 
 One step = the whole path over one batch of synthetic input:
-  fa_fwd (O, LSE)  ->  fa_bwd_preprocess (D)  ->  fa_bwd_dkdv  ->  fa_bwd_dq
+  fa_fwd (O, LSE)  ->  fa_bwd_dq (D, L log2 e, dQ)  ->  fa_bwd_dkdv (dK, dV)
 on B=1, H=64, N=8192, d=128, causal, bf16 (the N = 8192 workload the
 throughput target is stated at; forward-only workloads can be selected with
 --workload).  Inputs are seeded iid N(0,1) bf16 tensors already resident in
@@ -405,7 +405,7 @@ def main():
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
         ws = fa.workspace_for(B, H, N, causal, dev)
     stream = torch.cuda.current_stream()
-    names = ["fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if with_bwd else [])
+    names = ["fwd"] + (["bwd_dq", "bwd_dkdv"] if with_bwd else [])
 
     def step(ev=None):
         if ev is not None:
@@ -414,15 +414,12 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         if with_bwd:
-            fa.fa_bwd_preprocess(o, do, lse, ws, stream)
+            fa.fa_bwd_dq(q, k, v, o, do, lse, ws, dq, scale, causal, stream)
             if ev is not None:
                 ev[2].record(stream)
             fa.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, scale, causal, stream)
             if ev is not None:
                 ev[3].record(stream)
-            fa.fa_bwd_dq(q, k, v, do, ws, dq, scale, causal, stream)
-            if ev is not None:
-                ev[4].record(stream)
 
     flush_bytes = (args.flush_mib << 20) if not with_bwd else 0
     scratch = torch.empty(max(flush_bytes // 4, 1), dtype=torch.float32, device=dev)
@@ -523,7 +520,7 @@ def main():
         "fwd_hbm_gbps": acc.fwd_bytes(B, H, N, d) / (kern_ms["fwd"] * 1e-3) / 1e9,
     }
     if with_bwd:
-        bwd_ms = kern_ms["bwd_pre"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
+        bwd_ms = kern_ms["bwd_dq"] + kern_ms["bwd_dkdv"]
         bwd_tf = bwd_f / (bwd_ms * 1e-3) / 1e12
         out_extra.update({"bwd_ms": bwd_ms, "bwd_tflops": bwd_tf, "bwd_frac_of_peak": bwd_tf / peak})
     out_extra["kernel_ms"] = kern_ms
@@ -531,12 +528,30 @@ def main():
     out_extra["kernel_ms_min"] = {n: st["min"] for n, st in stats.items()}
     out_extra["clocks"] = {"before": clocks_before, "after": clocks_after}
     out_extra["power"] = power
+    if with_bwd:
+        # The standalone pre-pass (fa_bwd_preprocess: the same workspace the dQ
+        # stage writes), timed apart: it is not part of the step, whose dQ
+        # kernel computes D itself, but it is the HBM-bound form of that step.
+        ws2 = fa.workspace_for(B, H, N, causal, dev)
+        for _ in range(5):
+            fa.fa_bwd_preprocess(o, do, lse, ws2, stream)
+        pev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        pev[0].record(stream)
+        for _ in range(args.steps):
+            fa.fa_bwd_preprocess(o, do, lse, ws2, stream)
+        pev[1].record(stream)
+        torch.cuda.synchronize()
+        pre_ms = pev[0].elapsed_time(pev[1]) / args.steps
+        out_extra["bwd_preprocess_standalone"] = {
+            "ms": pre_ms, "hbm_gbps": acc.bwd_pre_bytes(B, H, N, d) / (pre_ms * 1e-3) / 1e9,
+            "peak_gbps": acc.MI355X_HBM_GBPS}
+        del ws2
 
     if args.hold > 0:
         out_extra["power_per_kernel"] = hold_kernels(torch, fa, stream, args.hold, {
             "fwd": lambda: fa.fa_fwd(q, k, v, o, lse, scale, causal, stream),
-            **({"bwd_dkdv": lambda: fa.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, scale, causal, stream),
-                "bwd_dq": lambda: fa.fa_bwd_dq(q, k, v, do, ws, dq, scale, causal, stream)}
+            **({"bwd_dq": lambda: fa.fa_bwd_dq(q, k, v, o, do, lse, ws, dq, scale, causal, stream),
+                "bwd_dkdv": lambda: fa.fa_bwd_dkdv(q, k, v, do, ws, dk, dv, scale, causal, stream)}
                if with_bwd else {})})
 
     # Roofline of the kernel that takes the most time per step.
@@ -544,9 +559,8 @@ def main():
     per_head_mm = 2.0 * N * N * d * half  # one N x N x d matmul, causal-halved
     work = {
         "fwd": ("mfma", 2 * per_head_mm * B * H, "fa_fwd: S = Q K^T and O = P V"),
-        "bwd_pre": ("hbm", acc.bwd_pre_bytes(B, H, N, d), "fa_bwd_preprocess: read O, dO, LSE; write D, L log2e"),
         "bwd_dkdv": ("mfma", 4 * per_head_mm * B * H, "fa_bwd_dkdv: S, dP, dV, dK matmuls"),
-        "bwd_dq": ("mfma", 3 * per_head_mm * B * H, "fa_bwd_dq: S, dP, dQ matmuls"),
+        "bwd_dq": ("mfma", 3 * per_head_mm * B * H, "fa_bwd_dq: S, dP, dQ matmuls (and D, L log2e)"),
     }
     dom = max(names, key=lambda n: kern_ms[n])
     bound, units, what = work[dom]

@@ -10,9 +10,9 @@ Functions mirror the C entry points:
   fa_fwd_split(q, k, v, o, lse, scale, causal)                 -> None
   fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale, causal, ws)   -> None
   fa_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, scale, causal) -> None
-  fa_bwd_preprocess(o, dO, lse, ws)                            -> None
+  fa_bwd_dq(q, k, v, o, dO, lse, ws, dq, scale, causal)        -> None
   fa_bwd_dkdv(q, k, v, dO, ws, dk, dv, scale, causal)          -> None
-  fa_bwd_dq(q, k, v, dO, ws, dq, scale, causal)                -> None
+  fa_bwd_preprocess(o, dO, lse, ws)                            -> None
   fa_bwd_workspace_size(B, H, N, d, causal)                    -> int
   fa_fp8_codes_size(B, H, N, d, layout), fa_fp8_exps_size(B, H, N, d) -> int
   fa_fp8_quantize(x, signs, codes, exps, layout)               -> None
@@ -71,7 +71,7 @@ def load_library() -> ctypes.CDLL:
         lib.fa_bwd_preprocess.restype = i
         lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, f, i, vp]
         lib.fa_bwd_dkdv.restype = i
-        lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, f, i, vp]
+        lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, f, i, vp]
         lib.fa_bwd_dq.restype = i
         lib.fa_fp8_codes_size.argtypes = [i, i, i, i, i]
         lib.fa_fp8_codes_size.restype = sz
@@ -203,13 +203,15 @@ def fa_bwd_dkdv(q, k, v, do, workspace, dk, dv, scale: float, causal: bool, stre
         raise FAError(st)
 
 
-def fa_bwd_dq(q, k, v, do, workspace, dq, scale: float, causal: bool, stream=None) -> None:
+def fa_bwd_dq(q, k, v, o, do, lse, workspace, dq, scale: float, causal: bool, stream=None) -> None:
     B, H, N, d = _shape(q)
-    for name, t in (("q", q), ("k", k), ("v", v), ("dO", do), ("dq", dq)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dO", do), ("dq", dq)):
         _check_tensor(name, t, torch.bfloat16, (B, H, N, d))
+    _check_tensor("lse", lse, torch.float32, (B, H, N))
     wp, wn = _ws(workspace)
-    st = load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), wp, wn, _ptr(dq), B, H, N, d,
-                                   float(scale), int(bool(causal)), _stream(stream))
+    st = load_library().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), wp, wn,
+                                   _ptr(dq), B, H, N, d, float(scale), int(bool(causal)),
+                                   _stream(stream))
     if st != FA_OK:
         raise FAError(st)
 

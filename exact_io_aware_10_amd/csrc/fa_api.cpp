@@ -102,20 +102,21 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, con
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
-              size_t workspace_bytes, void* dq, int B, int H, int N, int d, float scale, int causal,
-              void* stream) {
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
+              const float* lse, void* workspace, size_t workspace_bytes, void* dq, int B, int H,
+              int N, int d, float scale, int causal, void* stream) {
   bool empty = false;
   int st = check_common(B, H, N, d, scale, causal, &empty);
   if (st != FA_OK || empty) return st;
-  if (!q || !k || !v || !dO || !dq) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dO) || !aligned16(dq))
+  if (!q || !k || !v || !o || !dO || !lse || !dq) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
+      !aligned16(lse) || !aligned16(dq))
     return FA_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < fa_bwd_workspace_size(B, H, N, d, causal) ||
       !aligned16(workspace))
     return FA_ERR_WORKSPACE;
-  hipError_t e = fa::launch_bwd_dq(q, k, v, dO, static_cast<const float*>(workspace), dq, B, H, N,
-                                   scale, causal, static_cast<hipStream_t>(stream));
+  hipError_t e = fa::launch_bwd_dq(q, k, v, o, dO, lse, static_cast<float*>(workspace), dq, B, H,
+                                   N, scale, causal, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -133,9 +134,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
   float* ws = static_cast<float*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = fa::launch_bwd_pre(o, dO, lse, ws, B, H, N, s);
+  hipError_t e = fa::launch_bwd_dq(q, k, v, o, dO, lse, ws, dq, B, H, N, scale, causal, s);
   if (e == hipSuccess) e = fa::launch_bwd_dkdv(q, k, v, dO, ws, dk, dv, B, H, N, scale, causal, s);
-  if (e == hipSuccess) e = fa::launch_bwd_dq(q, k, v, dO, ws, dq, B, H, N, scale, causal, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -9,12 +9,16 @@
 // section "End-to-end flow": recompute each block's weights, then its
 // contribution to the Q, K and V gradients).
 //
-// Three launches, no atomics (bitwise deterministic):
-//   bwd_pre   workspace <- [-D = -rowsum(dO o O) | L log2(e)]   HBM-bound
+// Two launches, no atomics (bitwise deterministic):
+//   bwd_dq    per query block: Q, dO in registers; -D = -rowsum(dO o O) and
+//             L log2(e) of its rows computed from O, dO and LSE and written
+//             to the workspace; K, V tiles stream through LDS;
+//             dQ^T += K^T dS^T
 //   bwd_dkdv  per key block: K in registers, V in LDS; query tiles of Q, dO,
-//             L log2(e), -D stream through LDS; dV^T += dO^T P, dK^T += Q^T dS
-//   bwd_dq    per query block: Q, dO, L, -D held in registers; K, V tiles
-//             stream through LDS; dQ^T += K^T dS^T
+//             L log2(e), -D (from the workspace) stream through LDS;
+//             dV^T += dO^T P, dK^T += Q^T dS
+// (bwd_pre, exported as a stage of its own, fills the workspace exactly as
+// bwd_dq does, for callers that run the dK/dV kernel alone.)
 // Both kernels start each dP accumulation chain from -D instead of zero, so
 // their MFMAs produce dP - D and dS = P (dP - D) costs one multiply.
 // Tiles reach LDS through LDS-direct buffer loads; rows past N read as zero,
@@ -58,31 +62,37 @@ __device__ __forceinline__ void mfma_v_fence(f32x16& c0, f32x16& c1, f32x16& c2,
 }
 
 // ---------------------------------------------------------------------------
-// Pre-pass: -D_i = -sum_k dO_ik O_ik and L_i log2(e), 16 threads per row.
+// Pre-pass: -D_i = -sum_k dO_ik O_ik and L_i log2(e).  Summed exactly as the
+// dQ kernel sums them (lane h of a row takes dimensions 16 kc + 8 h .. + 7,
+// kc = 0..7, in that order; the two halves are then added), so both give the
+// same bits.  32 rows per wave.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float dot_bf16x8(u32x4 a, u32x4 b, float s) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    s = __builtin_fmaf(__uint_as_float(a[j] << 16), __uint_as_float(b[j] << 16), s);
+    s = __builtin_fmaf(__uint_as_float(a[j] & 0xffff0000u), __uint_as_float(b[j] & 0xffff0000u), s);
+  }
+  return s;
+}
+
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                       const uint16_t* __restrict__ dO,
                                                       const float* __restrict__ lse,
                                                       float* __restrict__ ws, int rows) {
-  const int gid = blockIdx.x * 256 + threadIdx.x;
-  const int row = gid >> 4;
-  const int part = gid & 15;
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 32 + (lane & 31);
   float s = 0.f;
   if (row < rows) {
-    const size_t off = (size_t)row * kD + part * 8;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(o + off);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + off);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float a0 = __uint_as_float(a[j] << 16), a1 = __uint_as_float(a[j] & 0xffff0000u);
-      const float b0 = __uint_as_float(b[j] << 16), b1 = __uint_as_float(b[j] & 0xffff0000u);
-      s = __builtin_fmaf(a0, b0, s);
-      s = __builtin_fmaf(a1, b1, s);
+    for (int kc = 0; kc < 8; ++kc) {
+      const size_t off = (size_t)row * kD + (2 * kc + h) * 8;
+      s = dot_bf16x8(*reinterpret_cast<const u32x4*>(o + off), *reinterpret_cast<const u32x4*>(dO + off), s);
     }
   }
-#pragma unroll
-  for (int w = 8; w >= 1; w >>= 1) s += __shfl_xor(s, w, 16);
-  if (row < rows && part == 0) {
+  s += __shfl_xor(s, 32);
+  if (row < rows && h == 0) {
     ws[row] = -s;
     ws[(size_t)rows + row] = lse[row] * kLog2e;
   }
@@ -539,8 +549,9 @@ __device__ __forceinline__ void s_fence2(f32x16& c0, f32x16& c1) {
 template <bool CAUSAL>
 __global__ __launch_bounds__(DQ_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                   const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
-                   const float* __restrict__ ws, uint16_t* __restrict__ dq, int BH, int N, int nqb,
+                   const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
+                   const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+                   float* __restrict__ ws, uint16_t* __restrict__ dq, int BH, int N, int nqb,
                    float sl2, float scale, uint32_t qkeep, uint32_t qflip) {
   __shared__ __attribute__((aligned(16))) char smem[DQ_SMEM];
   const uint32_t smem_lds = lds_addr(smem);
@@ -564,8 +575,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const rsrc_t rv = make_rsrc(v + head, head_bytes);
   const rsrc_t rdo = make_rsrc(dO + head, head_bytes);
   const size_t rows = (size_t)BH * N;
-  const rsrc_t rD = make_rsrc(ws + (size_t)bh * N, (uint32_t)N * 4);
-  const rsrc_t rL = make_rsrc(ws + rows + (size_t)bh * N, (uint32_t)N * 4);
+  const rsrc_t ro = make_rsrc(o + head, head_bytes);
+  const rsrc_t rL = make_rsrc(lse + (size_t)bh * N, (uint32_t)N * 4);
 
   // Q^T and dO^T as B operands (zero past N): lane holds
   // Q[q0w + 32 g + col][16 kc + 8 h .. + 7].  Q is negated for a negative
@@ -573,8 +584,10 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   // takes the signed scale at the store), then moved to AGPRs.  Both are
   // ordinary (compiler-tracked) loads, so that no copy of a fragment the
   // register allocator makes can run ahead of the data.
+  // O's fragments are loaded beside them (for D below), so that the three
+  // loads' latencies overlap.
   bf16x8 qf[2][8], df[2][8];
-  u32x4 qraw[2][8];
+  u32x4 qraw[2][8], oraw[2][8];
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -582,7 +595,11 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       const uint32_t off = (uint32_t)(q0w + 32 * g + col) * kRowBytes + (2 * kc + h) * 16;
       qraw[g][kc] = buf_load16(rq, off);
       df[g][kc] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
+      oraw[g][kc] = buf_load16(ro, off);
     }
+  float lraw[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) lraw[g] = buf_load_f32(rL, (uint32_t)(q0w + 32 * g + col) * 4);
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -590,14 +607,29 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       const bf16x8 qv = __builtin_bit_cast(bf16x8, signed_operand(qraw[g][kc], qkeep, qflip));
       asm volatile("" : "=a"(qf[g][kc]) : "0"(qv));
     }
+  // -D = -rowsum(dO o O) and L log2(e) of the lane's queries ("Interrogating
+  // the GPU, part 5", section "What does the backward pass do without P?":
+  // delta), summed as the pre-pass sums them (this lane's half of the
+  // dimensions in kc order, then the other half from lane ^ 32), and written
+  // to the workspace for the dK/dV kernel; rows past N read as zero.
   float l2[2], nd[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    l2[g] = buf_load_f32(rL, (uint32_t)(q0w + 32 * g + col) * 4);
-    nd[g] = buf_load_f32(rD, (uint32_t)(q0w + 32 * g + col) * 4);  // -D
+    const int qr = q0w + 32 * g + col;
+    float sd = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc)
+      sd = dot_bf16x8(oraw[g][kc], __builtin_bit_cast(u32x4, df[g][kc]), sd);
+    sd += __shfl_xor(sd, 32);
+    nd[g] = -sd;
+    l2[g] = lraw[g] * kLog2e;
+    if (h == 0 && qr < N) {
+      ws[(size_t)bh * N + qr] = nd[g];
+      ws[rows + (size_t)bh * N + qr] = l2[g];
+    }
   }
-  // Wait for L and -D here, in the compiler's view as well, before any
-  // LDS-direct load (invisible to it) is in flight.
+  // Wait for L here, in the compiler's view as well, before any LDS-direct
+  // load (invisible to it) is in flight.
   asm volatile("" : : "v"(l2[0]), "v"(l2[1]), "v"(nd[0]), "v"(nd[1]));
   // -D of the lane's query in every element: the dP^T chain starts from it,
   // so that its MFMAs produce dP - D and dS = P (dP - D) is one multiply.
@@ -843,7 +875,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* ws, int B, int H,
                           int N, hipStream_t stream) {
   const int rows = B * H * N;
-  hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows + 127) / 128)), dim3(256), 0,
                      stream, static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dO), lse,
                      ws, rows);
   return hipGetLastError();
@@ -865,9 +897,9 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
-                         const float* ws, void* dq, int B, int H, int N, float scale, int causal,
-                         hipStream_t stream) {
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                         const void* dO, const float* lse, float* ws, void* dq, int B, int H, int N,
+                         float scale, int causal, hipStream_t stream) {
   const int BH = B * H;
   const signed_scale sc = split_scale(scale, kSignBitsBf16);
   const float sl2 = sc.mag * kLog2e;
@@ -876,8 +908,8 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
   auto kern = causal ? bwd_dq_kernel<true> : bwd_dq_kernel<false>;
   hipLaunchKernelGGL(kern, grid, block, 0, stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                     static_cast<const uint16_t*>(dO), ws, static_cast<uint16_t*>(dq), BH, N, nqb,
-                     sl2, scale, sc.keep, sc.flip);
+                     static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dO), lse, ws,
+                     static_cast<uint16_t*>(dq), BH, N, nqb, sl2, scale, sc.keep, sc.flip);
   return hipGetLastError();
 }
 
@@ -887,8 +919,8 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
 // ends.  Host code never passes the array's name to a kernel (on the host it
 // is only a stand-in): the device address of each GPU's copy is looked up
 // once per device with hipGetSymbolAddress, with that device current, and
-// kept here.  Nothing in it needs clearing: the pre-pass writes every entry
-// the dK/dV and dQ kernels then read.  Calls that overlap on one GPU share
+// kept here.  Nothing in it needs clearing: the dQ kernel writes every entry
+// the dK/dV kernel then reads.  Calls that overlap on one GPU share
 // the array and race.
 // ---------------------------------------------------------------------------
 static __device__ __align__(256) char scratch[FA_NOALLOC_SCRATCH_BYTES];
@@ -917,9 +949,8 @@ hipError_t launch_bwd_noalloc(const void* q, const void* k, const void* v, const
     }
     ws = static_cast<float*>(g_scratch_addr[dev]);
   }
-  e = launch_bwd_pre(o, dO, lse, ws, B, H, N, stream);
+  e = launch_bwd_dq(q, k, v, o, dO, lse, ws, dq, B, H, N, scale, causal, stream);
   if (e == hipSuccess) e = launch_bwd_dkdv(q, k, v, dO, ws, dk, dv, B, H, N, scale, causal, stream);
-  if (e == hipSuccess) e = launch_bwd_dq(q, k, v, dO, ws, dq, B, H, N, scale, causal, stream);
   return e;
 }
 

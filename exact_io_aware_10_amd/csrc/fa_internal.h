@@ -47,9 +47,10 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
                            const float* ws, void* dk, void* dv, int B, int H, int N, float scale,
                            int causal, hipStream_t stream);
 
-hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
-                         const float* ws, void* dq, int B, int H, int N, float scale, int causal,
-                         hipStream_t stream);
+// dQ, and [-D | L log2(e)] of every row written into ws for the dK/dV kernel.
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                         const void* dO, const float* lse, float* ws, void* dq, int B, int H, int N,
+                         float scale, int causal, hipStream_t stream);
 
 // The backward with its workspace in the library's fixed per-GPU scratch
 // array (fa_bwd.hip); the caller has checked the size against it.

@@ -131,21 +131,24 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                    int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
- * The three stages fa_bwd runs, in order, on one stream.  Each is exposed so a
- * caller can schedule or time them separately; running all three with the
- * same arguments and workspace is exactly fa_bwd.  Arguments as for fa_bwd.
+ * The stages of the backward, each exposed so that a caller can schedule or
+ * time them separately.  fa_bwd runs fa_bwd_dq, then fa_bwd_dkdv, on one
+ * stream; running those two with the same arguments and workspace is exactly
+ * fa_bwd.  Arguments as for fa_bwd.
  *
- * fa_bwd_preprocess: fills the workspace with -D_i = -sum_k dO_ik O_ik, D
- *   being the row sum of dO o O that plays the role of delta in
- *   dS = P o (dP - delta) ("Interrogating the GPU, part 5", section "What
- *   does the backward pass do without P?"; stored negated because the other
- *   two stages start their dP accumulations from it), and with L_i log2(e)
- *   for the exp2-based recomputation.
- * fa_bwd_dkdv: for each key block, recompute P = exp(scale q.k - L) over all
- *   visible queries and accumulate dV = P^T dO and dK = scale dS^T Q.
- * fa_bwd_dq: for each query block, recompute P and dS over all visible keys
- *   and accumulate dQ = scale dS K.
- * The last two read the workspace the first one wrote.
+ * fa_bwd_dq: computes, for every query row, -D_i = -sum_k dO_ik O_ik (D plays
+ *   the role of delta in dS = P o (dP - delta), "Interrogating the GPU,
+ *   part 5", section "What does the backward pass do without P?"; stored
+ *   negated because both gradient stages start their dP accumulations from
+ *   it) and L_i log2(e) (for the exp2-based recomputation), writes them into
+ *   the workspace as [-D | L*log2(e)], and for each query block recomputes P
+ *   and dS over all visible keys and accumulates dQ = scale dS K.
+ * fa_bwd_dkdv: for each key block, recomputes P = exp(scale q.k - L) and dS
+ *   over all visible queries and accumulates dV = P^T dO and dK =
+ *   scale dS^T Q; it reads the workspace that fa_bwd_dq (or
+ *   fa_bwd_preprocess) wrote.
+ * fa_bwd_preprocess: writes the same workspace contents as fa_bwd_dq, bit
+ *   for bit, without computing dQ (for callers that need dK and dV alone).
  */
 int fa_bwd_preprocess(const void* o, const void* dO, const float* lse,
                       void* workspace, size_t workspace_bytes,
@@ -153,8 +156,8 @@ int fa_bwd_preprocess(const void* o, const void* dO, const float* lse,
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO,
                 const void* workspace, size_t workspace_bytes, void* dk, void* dv,
                 int B, int H, int N, int d, float scale, int causal, void* stream);
-int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO,
-              const void* workspace, size_t workspace_bytes, void* dq,
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
+              const float* lse, void* workspace, size_t workspace_bytes, void* dq,
               int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*

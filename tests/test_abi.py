@@ -107,7 +107,7 @@ def test_bwd_rejects_bad_workspace(fa):
     assert lib.fa_bwd(*p, 1, 1, 16, 128, 0.1, 1, FAKE + 4, 1 << 20, None) == fa.FA_ERR_WORKSPACE
     assert lib.fa_bwd_preprocess(FAKE, FAKE, FAKE, FAKE, 8, 1, 1, 16, 128, None) == fa.FA_ERR_WORKSPACE
     assert lib.fa_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, 1, 1, 16, 128, 0.1, 0, None) == fa.FA_ERR_WORKSPACE
-    assert lib.fa_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 1, 1, 16, 128, 0.1, 0, None) == fa.FA_ERR_WORKSPACE
+    assert lib.fa_bwd_dq(*([FAKE] * 6), FAKE, 8, FAKE, 1, 1, 16, 128, 0.1, 0, None) == fa.FA_ERR_WORKSPACE
 
 
 def test_bwd_rejects_bad_shapes(fa):

@@ -233,8 +233,10 @@ def test_graph_replays_match_eager(fa, entry):
 
 @pytest.mark.parametrize("shape", [(1, 3, 300), (2, 16, 4096)])
 def test_staged_backward_equals_fa_bwd(fa, shape):
-    """fa_bwd_preprocess -> fa_bwd_dkdv -> fa_bwd_dq (the calls bench.py times)
-    give exactly fa_bwd's gradients (both paths are deterministic)."""
+    """fa_bwd_dq -> fa_bwd_dkdv (the calls bench.py times) give exactly fa_bwd's
+    gradients; fa_bwd_preprocess writes the workspace bit for bit as
+    fa_bwd_dq does, so preprocess -> dkdv -> dq gives them too (every path
+    is deterministic)."""
     import torch
     B, H, N = shape
     x = fa_inputs.make(B, H, N, seed=9970 + N, with_do=True)
@@ -242,12 +244,21 @@ def test_staged_backward_equals_fa_bwd(fa, shape):
     o, lse = fa.forward(q, k, v, SCALE, True)
     dq, dk, dv = fa.backward(q, k, v, o, do, lse, SCALE, True)
     ws = fa.workspace_for(B, H, N, True, q.device)
+    ws2 = fa.workspace_for(B, H, N, True, q.device)
+    rows = B * H * N
     dq2, dk2, dv2 = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    fa.fa_bwd_preprocess(o, do, lse, ws)
+    fa.fa_bwd_dq(q, k, v, o, do, lse, ws, dq2, SCALE, True)
     fa.fa_bwd_dkdv(q, k, v, do, ws, dk2, dv2, SCALE, True)
-    fa.fa_bwd_dq(q, k, v, do, ws, dq2, SCALE, True)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    dq3, dk3, dv3 = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    fa.fa_bwd_preprocess(o, do, lse, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(ws2[: 8 * rows], ws[: 8 * rows])
+    fa.fa_bwd_dkdv(q, k, v, do, ws2, dk3, dv3, SCALE, True)
+    fa.fa_bwd_dq(q, k, v, o, do, lse, ws2, dq3, SCALE, True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq3) and torch.equal(dk, dk3) and torch.equal(dv, dv3)
 
 
 def test_error_paths_with_device_tensors(fa):
