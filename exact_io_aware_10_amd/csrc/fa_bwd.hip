@@ -62,12 +62,17 @@ __device__ __forceinline__ void mfma_v_fence(f32x16& c0, f32x16& c1, f32x16& c2,
 }
 
 // ---------------------------------------------------------------------------
-// Pre-pass: -D_i = -sum_k dO_ik O_ik and L_i log2(e).  Summed exactly as the
-// dQ kernel sums them (lane h of a row takes dimensions 16 kc + 8 h .. + 7,
-// kc = 0..7, in that order; the two halves are then added), so both give the
-// same bits.  32 rows per wave.
+// Pre-pass: -D_i = -sum_k dO_ik O_ik and L_i log2(e).  The sum runs in a
+// fixed order that the dQ kernel, which computes the same D in the step,
+// follows too, so both give the same bits: each 8-dimension chunk j is an fp32
+// chain of fused multiply-adds from zero (dimensions 8 j .. 8 j + 7 in order);
+// the chunks of one parity (j = 2 kc + h) are added in the tree
+// ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7)) over kc; the two parities
+// are added last.  Sixteen lanes per row, one 16-byte load of O and of dO
+// each; the tree is the xor-shuffles 2, 4, 8 (kc), then 1 (h).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float dot_bf16x8(u32x4 a, u32x4 b, float s) {
+__device__ __forceinline__ float dot_bf16x8(u32x4 a, u32x4 b) {
+  float s = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     s = __builtin_fmaf(__uint_as_float(a[j] << 16), __uint_as_float(b[j] << 16), s);
@@ -80,20 +85,19 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ dO,
                                                       const float* __restrict__ lse,
                                                       float* __restrict__ ws, int rows) {
-  const int lane = threadIdx.x & 63;
-  const int h = lane >> 5;
-  const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 32 + (lane & 31);
-  float s = 0.f;
+  const int t = threadIdx.x & 15;
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  float c = 0.f;
   if (row < rows) {
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      const size_t off = (size_t)row * kD + (2 * kc + h) * 8;
-      s = dot_bf16x8(*reinterpret_cast<const u32x4*>(o + off), *reinterpret_cast<const u32x4*>(dO + off), s);
-    }
+    const size_t off = (size_t)row * kD + t * 8;
+    c = dot_bf16x8(*reinterpret_cast<const u32x4*>(o + off), *reinterpret_cast<const u32x4*>(dO + off));
   }
-  s += __shfl_xor(s, 32);
-  if (row < rows && h == 0) {
-    ws[row] = -s;
+  c += __shfl_xor(c, 2);
+  c += __shfl_xor(c, 4);
+  c += __shfl_xor(c, 8);
+  c += __shfl_xor(c, 1);
+  if (row < rows && t == 0) {
+    ws[row] = -c;
     ws[(size_t)rows + row] = lse[row] * kLog2e;
   }
 }
@@ -609,17 +613,18 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     }
   // -D = -rowsum(dO o O) and L log2(e) of the lane's queries ("Interrogating
   // the GPU, part 5", section "What does the backward pass do without P?":
-  // delta), summed as the pre-pass sums them (this lane's half of the
-  // dimensions in kc order, then the other half from lane ^ 32), and written
-  // to the workspace for the dK/dV kernel; rows past N read as zero.
+  // delta), summed in the pre-pass's order (one chain per 8-dimension chunk,
+  // this lane's chunks kc = 0..7 added as a tree, then the other half of the
+  // dimensions from lane ^ 32), and written to the workspace for the dK/dV
+  // kernel; rows past N read as zero.
   float l2[2], nd[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     const int qr = q0w + 32 * g + col;
-    float sd = 0.f;
+    float c[8];
 #pragma unroll
-    for (int kc = 0; kc < 8; ++kc)
-      sd = dot_bf16x8(oraw[g][kc], __builtin_bit_cast(u32x4, df[g][kc]), sd);
+    for (int kc = 0; kc < 8; ++kc) c[kc] = dot_bf16x8(oraw[g][kc], __builtin_bit_cast(u32x4, df[g][kc]));
+    float sd = ((c[0] + c[1]) + (c[2] + c[3])) + ((c[4] + c[5]) + (c[6] + c[7]));
     sd += __shfl_xor(sd, 32);
     nd[g] = -sd;
     l2[g] = lraw[g] * kLog2e;
@@ -875,7 +880,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* ws, int B, int H,
                           int N, hipStream_t stream) {
   const int rows = B * H * N;
-  hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows + 127) / 128)), dim3(256), 0,
+  hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
                      stream, static_cast<const uint16_t*>(o), static_cast<const uint16_t*>(dO), lse,
                      ws, rows);
   return hipGetLastError();
