@@ -507,7 +507,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 // q0 + 64 w .. + 63 as two groups of 32, with their Q and dO fragments (the B
 // operands of S^T = K Q^T and dP^T = V dO^T) loaded once, Q into AGPRs, and
 // the dQ^T accumulators (128 registers) in AGPRs as well.  32-key tiles of K and V
-// stream through a four-slot LDS ring.  Owning 64 queries lets every K or V
+// stream through a five-slot LDS ring.  Owning 64 queries lets every K or V
 // fragment read from LDS feed two MFMAs.  Per tile t and wave:
 //   A  S^T  = K_t Q^T      16 MFMAs (VGPR accumulators, inline assembly)
 //   B  dP^T - D = V_t dO^T - D   16 MFMAs (the chain starts from -D of the
@@ -524,10 +524,12 @@ constexpr int DQ_TILE = DQ_BK * kRowBytes;   // 8 KiB (K or V)
 constexpr int DQ_THREADS = DQ_WAVES * 64;
 constexpr int DQ_TLOADS = DQ_TILE / 1024 / DQ_WAVES;  // LDS-direct loads per wave per tensor
 constexpr int DQ_SLOT = 2 * DQ_TILE;                  // K tile, then V tile
-constexpr int DQ_NSLOT = 4;
-constexpr int DQ_SMEM = DQ_NSLOT * DQ_SLOT;           // 64 KiB
+constexpr int DQ_NSLOT = 5;
+constexpr int DQ_SMEM = DQ_NSLOT * DQ_SLOT;           // 80 KiB
 constexpr int DQ_LOADS_PER_TILE = 2 * DQ_TLOADS;
 constexpr int DQ_AHEAD = 3;                           // LDS read-ahead of phases A and B, in k-steps
+constexpr int DQ_CA = 3;                              // LDS read-ahead of phase C, in product steps
+constexpr int DQ_CPRE = 4;                            // phase B k-step after which phase C's first reads issue
 
 // S^T / dP^T MFMA with the B operand (Q^T or dO^T) in AGPRs and the result in
 // VGPRs; hazards as for mfma_v (s_fence2 after the last one).
@@ -702,7 +704,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       for (int i = 0; i < 16; ++i) acc[g][mb][i] = 0.f;
 
   // dS^T of the previous tile as B operands [group][key half]; zero before the
-  // first tile, whose products read the K part of slot 3, cleared below.
+  // first tile, whose products read the K part of the last slot, cleared below.
   bf16x8 sb[2][2];
 #pragma unroll
   for (int g = 0; g < 2; ++g)
@@ -723,24 +725,28 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     }
   };
 
-  // dQ^T += K^T dS^T for the tile in slot psl (phase C), with sb.
+  // dQ^T += K^T dS^T for the tile in slot psl (phase C), with sb.  Its K^T
+  // fragments are read DQ_CA product steps (2 DQ_CA MFMAs) ahead, the first
+  // DQ_CA of them by dq_prefetch, which the step issues during phase B.
+  bf16x8 ca[DQ_CA + 1];
+  auto rdt = [&](int psl, int n) {
+    const char* rb = smem + psl * DQ_SLOT + 16 * (n >> 2) * kRowBytes;
+    const int mb = n & 3;
+    ca[n % (DQ_CA + 1)] = join(lds_read_tr(rb + troff[mb][0]), lds_read_tr(rb + troff[mb][1]));
+  };
+  auto dq_prefetch = [&](int psl) {
+#pragma unroll
+    for (int n = 0; n < DQ_CA; ++n) rdt(psl, n);
+  };
   auto dq_products = [&](int psl, auto&& between) {
-    const char* kt = smem + psl * DQ_SLOT;
-    bf16x8 a[2];
-    auto rdt = [&](int n, int b) {
-      const int mb = n & 3, u = n >> 2;
-      const char* rb = kt + 16 * u * kRowBytes;
-      a[b] = join(lds_read_tr(rb + troff[mb][0]), lds_read_tr(rb + troff[mb][1]));
-    };
-    rdt(0, 0);
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      const int b = n & 1, mb = n & 3, u = n >> 2;
-      if (n < 7) rdt(n + 1, b ^ 1);
+      const int b = n % (DQ_CA + 1), mb = n & 3, u = n >> 2;
+      if (n + DQ_CA < 8) rdt(psl, n + DQ_CA);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        mfma_aa(acc[g][mb], a[b], sb[g][u]);
+        mfma_aa(acc[g][mb], ca[b], sb[g][u]);
         between(2 * n + g);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -750,28 +756,37 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     acc_fence8(acc);
   };
 
-  // Step t (slot SL = t % 4, a compile-time constant so that every LDS
-  // offset into the slot folds into the instructions): phases A, B, C as
-  // described above; the dQ products of phase C belong to tile t - 1 (zero dS
-  // before the first tile).
+  // The ring: tile j is in slot j % 5.  The barrier W(j) (ring_wait_barrier)
+  // waits until this wave's loads of tile j have landed (only tile j + 1's
+  // may still be in flight), publishes every wave's part of it, and is
+  // followed by the loads of tile j + 2.  Every wave passes W(0) .. W(nt).
+  // K fragments of phase A, read DQ_AHEAD k-steps before their MFMAs (two
+  // MFMAs per step are too short to cover the LDS latency); the first
+  // DQ_AHEAD of a tile are read before the previous step's phase C, so that
+  // its MFMAs cover their latency.
+  bf16x8 ka[DQ_AHEAD + 1];
+  auto ka_prefetch = [&](int sl) {
+#pragma unroll
+    for (int j = 0; j < DQ_AHEAD; ++j) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(smem + sl * DQ_SLOT, roff[j]));
+  };
+
+  // Step t (slot SL = t % 5, a compile-time constant so that every LDS
+  // offset into the slot folds into the instructions): phases A and B of
+  // tile t; then W(t + 1), whose barrier also frees the slot of tile t - 2
+  // (last read in the previous step's phase C) for tile t + 3; then phase C,
+  // the dQ products of tile t - 1 (zero dS before the first tile), whose
+  // slot the new loads do not touch.
   auto step = [&](int t, auto slc) {
     constexpr int SL = decltype(slc)::value;
     constexpr int PSL = (SL + DQ_NSLOT - 1) % DQ_NSLOT;
-    // Tile t has landed once only tile t + 1's loads may be in flight; the
-    // barrier publishes it and frees the slot of tile t - 2, which tile t + 2
-    // takes (tile t - 1 is still read here, in phase C).
-    ring_wait_barrier<DQ_LOADS_PER_TILE>();
-    issue_tile(t + 2, (SL + 2) % DQ_NSLOT);
+    constexpr int NSL = (SL + 1) % DQ_NSLOT;
     const char* kb = smem + SL * DQ_SLOT;
     const char* vb = kb + DQ_TILE;
 
-    // Phase A: S^T for both query groups.  K and V fragments are read
-    // DQ_AHEAD k-steps before their MFMAs (two MFMAs per step are too short
-    // to cover the LDS latency); V's first ones during the last K steps.
+    // Phase A: S^T for both query groups; V's first fragments are read
+    // during the last K steps.
     f32x16 s[2], dp[2];
-    bf16x8 ka[DQ_AHEAD + 1], va[DQ_AHEAD + 1];
-#pragma unroll
-    for (int j = 0; j < DQ_AHEAD; ++j) ka[j] = __builtin_bit_cast(bf16x8, lds_read16(kb, roff[j]));
+    bf16x8 va[DQ_AHEAD + 1];
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       const int b = kc % (DQ_AHEAD + 1);
@@ -814,8 +829,14 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         asm volatile("" : "+v"(s[sg][si]), "+v"(s[sg][si + 1]));
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (kc == DQ_CPRE) dq_prefetch(PSL);
+      __builtin_amdgcn_sched_barrier(0);
     }
     s_fence2(dp[0], dp[1]);
+
+    ring_wait_barrier<DQ_LOADS_PER_TILE>();  // W(t + 1)
+    issue_tile(t + 3, (SL + 3) % DQ_NSLOT);
+    if (t + 1 < tw) ka_prefetch(NSL);
 
     // Phase C: dQ products of tile t - 1, with dS = P (dP - D) of tile t in
     // between, packed into the next step's B operands.
@@ -835,25 +856,34 @@ void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         sb[g][u] = __builtin_bit_cast(bf16x8, u32x4{w[g][4 * u], w[g][4 * u + 1], w[g][4 * u + 2], w[g][4 * u + 3]});
   };
 
-  // Slot 3 feeds the first step's dQ products: clear its K tile.
+  // The last slot (that of tile -1) feeds the first step's dQ products:
+  // clear its K tile (published by W(0)).
   {
-    char* z = smem + 3 * DQ_SLOT;
+    char* z = smem + (DQ_NSLOT - 1) * DQ_SLOT;
     for (int o = tid * 16; o < DQ_TILE; o += DQ_THREADS * 16) lds_write16(z, o, u32x4{0u, 0u, 0u, 0u});
   }
   issue_tile(0, 0);
   issue_tile(1, 1);
-  for (int t = 0; t < tw; t += 4) {
+  ring_wait_barrier<DQ_LOADS_PER_TILE>();  // W(0)
+  issue_tile(2, 2);
+  if (tw > 0) ka_prefetch(0);
+  static_assert(DQ_NSLOT == 5, "the step loop is unrolled over the five slots");
+  for (int t = 0; t < tw; t += 5) {
     step(t, kv_ic<0>{});
     if (t + 1 < tw) step(t + 1, kv_ic<1>{});
     if (t + 2 < tw) step(t + 2, kv_ic<2>{});
     if (t + 3 < tw) step(t + 3, kv_ic<3>{});
+    if (t + 4 < tw) step(t + 4, kv_ic<4>{});
   }
-  // Step tw: the last tile's dQ products; then the wave only keeps the ring
-  // going up to the workgroup's step nt.
-  for (int tt = tw; tt <= nt; ++tt) {
+  // The last tile's dQ products (its slot is refilled only at W(tw + 2));
+  // then the wave only keeps the ring going up to the workgroup's W(nt).
+  if (tw > 0) {
+    dq_prefetch((tw - 1) % DQ_NSLOT);
+    dq_products((tw - 1) % DQ_NSLOT, [](int) {});
+  }
+  for (int tt = tw + 1; tt <= nt; ++tt) {
     ring_wait_barrier<DQ_LOADS_PER_TILE>();
     issue_tile(tt + 2, (tt + 2) % DQ_NSLOT);
-    if (tt == tw && tw > 0) dq_products((tw - 1) % DQ_NSLOT, [](int) {});
   }
   dma_drain();  // no LDS-direct load may outlive the workgroup
 

@@ -159,10 +159,12 @@ void mix1(const u32x4* __restrict__ src, float* __restrict__ out, long long* __r
 //   2  A held for four MFMAs
 //   3  B held for four MFMAs, A changes every MFMA
 //   4  A and B both held for four MFMAs (four accumulators)
+//   5  as 0, but each accumulator takes two consecutive MFMAs
+//   6  as 0, but each accumulator takes four consecutive MFMAs (two in use)
 template <int ORDER>
 __device__ __forceinline__ void order_ops(int n, int i, int& ai, int& bi) {
   // n: half of the iteration (0, 1); i: MFMA within the half (0..3)
-  if (ORDER == 0) {
+  if (ORDER == 0 || ORDER >= 5) {
     ai = n ? (i ^ 2) : i;
     bi = n ? (i ^ 3) : (i ^ 1);
   } else if (ORDER == 1) {
@@ -201,7 +203,8 @@ __global__ __launch_bounds__(256) void mfma_order(const u32x4* __restrict__ src,
       for (int i = 0; i < 4; ++i) {
         int ai, bi;
         order_ops<ORDER>(n, i, ai, bi);
-        c[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ai], b[bi], c[i], 0, 0, 0);
+        const int ci = ORDER == 5 ? 2 * n + (i >> 1) : ORDER == 6 ? n : i;
+        c[ci] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ai], b[bi], c[ci], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
   }
@@ -384,7 +387,8 @@ __global__ __launch_bounds__(256) void atomic_rate(float* __restrict__ dst, int 
 // LDS array read in a loop, eight reads per iteration, each a wave-wide
 // contiguous span; the base offset moves every iteration through a register
 // the compiler cannot follow, so no read can be hoisted out of the loop.
-// KIND 0: ds_read_b128, 1: ds_read_b64, 2: ds_read_b64_tr_b16.  cyc gets
+// KIND 0: ds_read_b128, 1: ds_read_b64, 2: ds_read_b64_tr_b16, 3: ds_read_b128
+// with every lane of a wave at the same address (a broadcast).  cyc gets
 // each wave's s_memtime cycles.
 constexpr int kLdsWords = 16384;  // 64 KiB of u32
 template <int KIND>
@@ -397,18 +401,18 @@ __global__ __launch_bounds__(512) void lds_rate(unsigned* __restrict__ out, long
   for (int i = tid; i < kLdsWords; i += 512) buf[i] = (unsigned)i * 2654435761u;
   __syncthreads();
   const char* base = reinterpret_cast<const char*>(buf);
-  constexpr int kBytes = KIND == 0 ? 16 : 8;  // per lane and read
+  constexpr int kBytes = (KIND == 0 || KIND == 3) ? 16 : 8;  // per lane and read
   constexpr int kSpan = 64 * kBytes;          // per wave and read
   constexpr int kMask = kLdsWords * 4 - 1;
   unsigned x = 0;
-  int b = wave * kSpan + lane * kBytes;
+  int b = wave * kSpan + (KIND == 3 ? 0 : lane * kBytes);
   const long long t0 = __builtin_amdgcn_s_memtime();
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       // wave-wide span u of this iteration, wrapped inside the 64 KiB array
       const int off = (b + u * 8 * kSpan) & kMask;
-      if (KIND == 0) {
+      if (KIND == 0 || KIND == 3) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(base + off);
         x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
       } else if (KIND == 1) {
@@ -575,17 +579,19 @@ int main(int argc, char** argv) {
   if (!*only || !strcmp(only, "order")) {
     CHECK(hipMemcpy(src, rnd.data(), nfrag * 16, hipMemcpyHostToDevice));
     const telemetry tel;
-    const char* names[5] = {"no operand shared", "A held for 2", "A held for 4", "B held for 4",
-                            "A and B held for 4"};
+    const char* names[7] = {"no operand shared", "A held for 2", "A held for 4", "B held for 4",
+                            "A and B held for 4", "accumulator held for 2", "accumulator held for 4"};
     const int grid = 2 * kCUs, iters = 20000, launches = 160;  // about a second per variant
-    for (int order = 0; order < 5; ++order) {
+    for (int order = 0; order < 7; ++order) {
       auto launch = [&](int it) {
         switch (order) {
           case 0: hipLaunchKernelGGL(mfma_order<0>, dim3(grid), dim3(256), 0, 0, src, out, it); break;
           case 1: hipLaunchKernelGGL(mfma_order<1>, dim3(grid), dim3(256), 0, 0, src, out, it); break;
           case 2: hipLaunchKernelGGL(mfma_order<2>, dim3(grid), dim3(256), 0, 0, src, out, it); break;
           case 3: hipLaunchKernelGGL(mfma_order<3>, dim3(grid), dim3(256), 0, 0, src, out, it); break;
-          default: hipLaunchKernelGGL(mfma_order<4>, dim3(grid), dim3(256), 0, 0, src, out, it); break;
+          case 4: hipLaunchKernelGGL(mfma_order<4>, dim3(grid), dim3(256), 0, 0, src, out, it); break;
+          case 5: hipLaunchKernelGGL(mfma_order<5>, dim3(grid), dim3(256), 0, 0, src, out, it); break;
+          default: hipLaunchKernelGGL(mfma_order<6>, dim3(grid), dim3(256), 0, 0, src, out, it); break;
         }
       };
       launch(100);
@@ -793,6 +799,92 @@ int main(int argc, char** argv) {
     printf("{\"probe\": \"atomic_dq_b1_h64_n8192_causal\", \"atomic_bytes\": %.0f, \"ms\": %.3f, "
            "\"gbps\": %.0f, \"result_checked\": %s}\n", adds * 4, ms, adds * 4 / ms / 1e6, ok ? "true" : "false");
     CHECK(hipFree(dq));
+  }
+  if (!*only || !strcmp(only, "power")) {
+    // Board power and clock while one instruction kind runs alone on every
+    // CU for about a second: wave instructions per second, and the power
+    // above the idle reading divided by that rate (energy per wave
+    // instruction at the clock the board settles at).
+    CHECK(hipMemcpy(src, rnd.data(), nfrag * 16, hipMemcpyHostToDevice));
+    const telemetry tel;
+    unsigned* lout;
+    long long* lcyc;
+    CHECK(hipMalloc(&lout, (size_t)kCUs * 512 * sizeof(unsigned)));
+    CHECK(hipMalloc(&lcyc, (size_t)kCUs * 8 * sizeof(long long)));
+    CHECK(hipDeviceSynchronize());
+    std::this_thread::sleep_for(std::chrono::milliseconds(1000));
+    double idle = 0;
+    for (int i = 0; i < 20; ++i) {
+      idle += tel.power_w();
+      std::this_thread::sleep_for(std::chrono::milliseconds(10));
+    }
+    idle /= 20;
+    const char* names[8] = {"v_fma_f32", "v_exp_f32 + v_add_f32", "ds_read_b128 (+4 v_xor_b32 per read)",
+                            "v_mfma_f32_32x32x16_bf16 random operands", "v_mfma_f32_32x32x16_bf16 constant operands",
+                            "ds_read_b64 (+2 v_xor_b32 per read)", "ds_read_b64_tr_b16 (+1 v_xor_b32 per read)",
+                            "ds_read_b128 broadcast, one address per wave (+4 v_xor_b32 per read)"};
+    for (int kind = 0; kind < 8; ++kind) {
+      const int vgrid = 2 * kCUs, viters = 20000, liters = 4096, miters = 20000;
+      double per_launch = 0;  // wave instructions of the measured kind per launch
+      auto launch = [&]() {
+        switch (kind) {
+          case 0: hipLaunchKernelGGL(valu_rate<0>, dim3(vgrid), dim3(256), 0, 0, out, cyc, viters);
+                  per_launch = (double)vgrid * 4 * viters * 16; break;
+          case 1: hipLaunchKernelGGL(valu_rate<1>, dim3(vgrid), dim3(256), 0, 0, out, cyc, viters);
+                  per_launch = (double)vgrid * 4 * viters * 16; break;
+          case 2: hipLaunchKernelGGL(lds_rate<0>, dim3(kCUs), dim3(512), 0, 0, lout, lcyc, liters);
+                  per_launch = (double)kCUs * 8 * liters * 8; break;
+          case 5: hipLaunchKernelGGL(lds_rate<1>, dim3(kCUs), dim3(512), 0, 0, lout, lcyc, liters);
+                  per_launch = (double)kCUs * 8 * liters * 8; break;
+          case 6: hipLaunchKernelGGL(lds_rate<2>, dim3(kCUs), dim3(512), 0, 0, lout, lcyc, liters);
+                  per_launch = (double)kCUs * 8 * liters * 8; break;
+          case 7: hipLaunchKernelGGL(lds_rate<3>, dim3(kCUs), dim3(512), 0, 0, lout, lcyc, liters);
+                  per_launch = (double)kCUs * 8 * liters * 8; break;
+          default: hipLaunchKernelGGL(mfma_order<0>, dim3(vgrid), dim3(256), 0, 0, src, out, miters);
+                  per_launch = (double)vgrid * 4 * miters * 8; break;
+        }
+      };
+      if (kind == 3) CHECK(hipMemcpy(src, rnd.data(), nfrag * 16, hipMemcpyHostToDevice));
+      if (kind == 4) CHECK(hipMemcpy(src, one.data(), nfrag * 16, hipMemcpyHostToDevice));
+      CHECK(hipEventRecord(e0));
+      launch();
+      CHECK(hipEventRecord(e1));
+      CHECK(hipDeviceSynchronize());
+      const int launches = std::max(1, (int)(1000.0 / std::max(time_ms(e0, e1), 0.01f)));
+      std::this_thread::sleep_for(std::chrono::milliseconds(500));
+      std::atomic<bool> stop{false};
+      std::vector<double> pw, sc;
+      std::thread sampler([&] {
+        while (!stop.load()) {
+          pw.push_back(tel.power_w());
+          sc.push_back(tel.sclk_mhz());
+          std::this_thread::sleep_for(std::chrono::milliseconds(10));
+        }
+      });
+      CHECK(hipEventRecord(e0));
+      for (int l = 0; l < launches; ++l) launch();
+      CHECK(hipEventRecord(e1));
+      CHECK(hipDeviceSynchronize());
+      stop = true;
+      sampler.join();
+      const double ms = time_ms(e0, e1);
+      double p = 0, c = 0;
+      size_t n0 = pw.size() / 2, n = 0;
+      for (size_t i = n0; i < pw.size(); ++i, ++n) {
+        p += pw[i];
+        c += sc[i];
+      }
+      p = n ? p / n : -1;
+      c = n ? c / n : -1;
+      const double rate = per_launch * launches / (ms * 1e-3);  // wave instructions per second
+      printf("{\"probe\": \"power\", \"instruction\": \"%s\", \"ms\": %.1f, \"giga_wave_instructions_per_s\": %.2f, "
+             "\"power_w\": %.1f, \"idle_w\": %.1f, \"sclk_mhz\": %.0f, \"nj_per_wave_instruction_above_idle\": %.3f, "
+             "\"samples\": %zu}\n",
+             names[kind], ms, rate / 1e9, p, idle, c, (p - idle) / rate * 1e9, n);
+      fflush(stdout);
+    }
+    CHECK(hipFree(lout));
+    CHECK(hipFree(lcyc));
   }
   CHECK(hipFree(src));
   CHECK(hipFree(out));
