@@ -272,6 +272,33 @@ def kernel_stats(samples):
             "min": min(samples)}
 
 
+def soft_exp2_forward(fa, torch, q, k, v, o, lse, scale, causal, B, H, N, d, stream, warmup: int,
+                      steps: int):
+    """The row-block forward with 0, 8, 16 or 32 of each lane's 32 exponentials
+    per tile evaluated in software (fa_fwd_soft_exp2; "Interrogating the GPU,
+    part 5", FlashAttention-4 section), on the same inputs and outputs as the
+    step, each share timed over `steps` launches with HIP events on the
+    launch stream after `warmup` untimed ones.  Not part of the step or of
+    `value`: it measures whether moving exponentials to the FMA path pays
+    on this GPU."""
+    flops = acc.fwd_flops(B, H, N, d, causal)
+    out = {}
+    for share in (0, 8, 16, 32):
+        for _ in range(max(warmup, 5)):
+            fa.fa_fwd_soft_exp2(q, k, v, o, lse, scale, causal, share, stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(steps):
+            fa.fa_fwd_soft_exp2(q, k, v, o, lse, scale, causal, share, stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / steps
+        out[str(share)] = {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+                           "frac_of_peak": flops / (ms * 1e-3) / 1e12 / acc.MI355X_BF16_DENSE_TFLOPS}
+    return {"kernel": "row-block forward, share of 32 exponentials per tile in software",
+            "by_share": out}
+
+
 def fp8_forward(fa, torch, q, k, v, w, workload, stream, warmup: int, steps: int):
     """The FP8 forward (incoherent processing) on the same Q, K, V: rotate and
     quantise Q, K, V (three launches), then FP8 attention.  Timed apart from
@@ -341,6 +368,8 @@ def main():
                          "256 MB last-level cache (0: no flush; the K steps then run as one graph)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward timing")
+    ap.add_argument("--no-soft-exp2", action="store_true",
+                    help="skip the timing of the forward with software exponentials")
     ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
                     help="time the K steps as one HIP graph replay (auto: for forward-only "
                          "workloads, whose microsecond kernels would otherwise wait on the host)")
@@ -584,6 +613,13 @@ def main():
         log(f"fp8 forward: quantise {fp8['quantize_ms']:.3f} ms, attention {fp8['attn_ms']:.3f} ms "
             f"({fp8['attn_tflops']:.0f} TFLOP/s credited)")
 
+    soft = None
+    if not args.no_soft_exp2:
+        soft = soft_exp2_forward(fa, torch, q, k, v, o, lse, scale, causal, B, H, N, d, stream,
+                                 args.warmup, args.steps)
+        log("forward with software exponentials (share of 32 per tile: ms): "
+            + ", ".join(f"{s_}: {r['ms']:.4f}" for s_, r in soft["by_share"].items()))
+
     cpu = None
     if not args.no_cpu_baseline:
         heads = args.cpu_heads or CPU_SAMPLE_HEADS[args.workload]
@@ -614,6 +650,7 @@ def main():
         **out_extra,
         "roofline": roof,
         "fp8_forward": fp8,
+        "fwd_soft_exp2": soft,
         "cpu_baseline": cpu,
         "source_hash": source_hash(),
     }

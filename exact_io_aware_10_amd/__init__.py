@@ -8,6 +8,7 @@ built, or the tensors are not on a ROCm device, the calls raise.
 Functions mirror the C entry points:
   fa_fwd(q, k, v, o, lse, scale, causal)                       -> None
   fa_fwd_split(q, k, v, o, lse, scale, causal)                 -> None
+  fa_fwd_soft_exp2(q, k, v, o, lse, scale, causal, share)      -> None
   fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale, causal, ws)   -> None
   fa_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, scale, causal) -> None
   fa_bwd_dq(q, k, v, o, dO, lse, ws, dq, scale, causal)        -> None
@@ -61,6 +62,8 @@ def load_library() -> ctypes.CDLL:
         lib.fa_fwd.restype = i
         lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         lib.fa_fwd_split.restype = i
+        lib.fa_fwd_soft_exp2.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+        lib.fa_fwd_soft_exp2.restype = i
         lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
         lib.fa_bwd_workspace_size.restype = sz
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
@@ -141,6 +144,17 @@ def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
 
 def fa_fwd_split(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
     _fwd_call("fa_fwd_split", q, k, v, o, lse, scale, causal, stream)
+
+
+def fa_fwd_soft_exp2(q, k, v, o, lse, scale: float, causal: bool, share: int, stream=None) -> None:
+    B, H, N, d = _shape(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_tensor(name, t, torch.bfloat16, (B, H, N, d))
+    _check_tensor("lse", lse, torch.float32, (B, H, N))
+    st = load_library().fa_fwd_soft_exp2(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+                                         float(scale), int(bool(causal)), int(share), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st)
 
 
 def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, workspace,

@@ -62,6 +62,23 @@ int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* ls
   return checked_fwd(fa::launch_fwd_split, q, k, v, o, lse, B, H, N, d, scale, causal, stream);
 }
 
+int fa_fwd_soft_exp2(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int N, int d, float scale, int causal, int software_share,
+                     void* stream) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, causal, &empty);
+  if (st != FA_OK) return st;
+  if (software_share != 0 && software_share != 8 && software_share != 16 && software_share != 32)
+    return FA_ERR_INVALID_ARG;
+  if (empty) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_UNSUPPORTED;
+  hipError_t e = fa::launch_fwd_soft_exp2(q, k, v, o, lse, B, H, N, scale, causal, software_share,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal) {
   bool empty = false;
   if (check_common(B, H, N, d, 1.f, causal, &empty) != FA_OK) return 0;

@@ -51,7 +51,33 @@ constexpr float kTau = 8.f;
 template <int V>
 using ic = std::integral_constant<int, V>;
 
-template <bool CAUSAL>
+// 2^x on the FMA path instead of the transcendental unit ("Interrogating the
+// GPU, part 5: FlashAttention", section "Why did Blackwell need
+// FlashAttention-4?": part of the exponentials evaluated in software):
+// x = n + f with n = floor(x) and f in [0, 1), 2^f from the page's cubic
+// 1 + 0.6951 f + 0.2276 f^2 + 0.0771 f^3 (relative error about 1e-4 on
+// [0, 1)), and n added to the exponent field of the result.  Arguments here
+// are at most kTau (the stale maximum bounds the scores), so 2^n stays
+// normal; below -126 (masked scores are -inf) the result is 0.  Ten
+// full-rate VALU instructions against one v_exp_f32.
+__device__ __forceinline__ float soft_exp2(float x) {
+  const float xc = fmaxf(x, -126.f);
+  const float fl = __builtin_floorf(xc);
+  const float f = xc - fl;
+  const float p = __builtin_fmaf(__builtin_fmaf(__builtin_fmaf(0.0771f, f, 0.2276f), f, 0.6951f), f, 1.f);
+  const float r = __int_as_float(__float_as_int(p) + ((int)fl << 23));
+  return x >= -126.f ? r : 0.f;
+}
+
+// SW of a lane's 32 exponentials per tile (0, 8, 16 or 32) go through
+// soft_exp2, spread evenly over the tile: element e = 16 st + i when
+// e % (32 / SW) == 0.
+template <int SW>
+__device__ __forceinline__ constexpr bool soft_elem(int e) {
+  return SW > 0 && e % (32 / SW) == 0;
+}
+
+template <bool CAUSAL, int SW = 0>
 __global__ __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
@@ -215,7 +241,8 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(__builtin_fmaf(s[st][i], sl2, -mu));
+          const float x = __builtin_fmaf(s[st][i], sl2, -mu);
+          const float p = soft_elem<SW>(16 * st + i) ? soft_exp2(x) : fast_exp2(x);
           s[st][i] = p;
           rs += p;
         }
@@ -561,6 +588,38 @@ hipError_t launch_fwd_rows(const void* q, const void* k, const void* v, void* o,
     hipLaunchKernelGGL(fwd_kernel<true>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2, sc.keep, sc.flip);
   else
     hipLaunchKernelGGL(fwd_kernel<false>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2, sc.keep, sc.flip);
+  return hipGetLastError();
+}
+
+template <int SW>
+static void launch_rows_sw(dim3 grid, dim3 block, hipStream_t stream, int causal, const uint16_t* qq,
+                           const uint16_t* kk, const uint16_t* vv, uint16_t* oo, float* lse, int BH,
+                           int N, int nqb, float sl2, signed_scale sc) {
+  if (causal)
+    hipLaunchKernelGGL((fwd_kernel<true, SW>), grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2, sc.keep, sc.flip);
+  else
+    hipLaunchKernelGGL((fwd_kernel<false, SW>), grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2, sc.keep, sc.flip);
+}
+
+hipError_t launch_fwd_soft_exp2(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int N, float scale, int causal, int share,
+                                hipStream_t stream) {
+  const int BH = B * H;
+  const int nqb = (N + FWD_BR - 1) / FWD_BR;
+  const signed_scale sc = split_scale(scale, kSignBitsBf16);
+  const float sl2 = sc.mag * kLog2e;
+  dim3 grid((unsigned)(nqb * BH)), block(FWD_THREADS);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  uint16_t* oo = static_cast<uint16_t*>(o);
+  switch (share) {
+    case 0: launch_rows_sw<0>(grid, block, stream, causal, qq, kk, vv, oo, lse, BH, N, nqb, sl2, sc); break;
+    case 8: launch_rows_sw<8>(grid, block, stream, causal, qq, kk, vv, oo, lse, BH, N, nqb, sl2, sc); break;
+    case 16: launch_rows_sw<16>(grid, block, stream, causal, qq, kk, vv, oo, lse, BH, N, nqb, sl2, sc); break;
+    case 32: launch_rows_sw<32>(grid, block, stream, causal, qq, kk, vv, oo, lse, BH, N, nqb, sl2, sc); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

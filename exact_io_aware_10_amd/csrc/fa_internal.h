@@ -38,6 +38,11 @@ hipError_t launch_fwd_rows(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int N, float scale, int causal, hipStream_t stream);
 hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int H, int N, float scale, int causal, hipStream_t stream);
+// The row-block kernel with `share` (0, 8, 16 or 32) of each lane's 32
+// exponentials per tile computed on the FMA path (soft_exp2).
+hipError_t launch_fwd_soft_exp2(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int N, float scale, int causal, int share,
+                                hipStream_t stream);
 
 // Backward workspace layout (2 B*H*N floats): [-D = -rowsum(dO * O) | L * log2(e)].
 hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* ws, int B, int H,

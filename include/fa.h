@@ -69,8 +69,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * The forward pass through its key-split kernel, whatever the sizes.  fa_fwd
- * runs it by itself when B * H * ceil(N / 128) is below 128 (below 256 when
- * causal), i.e. when one workgroup per 128 query rows leaves most of the
+ * runs it by itself when B * H * ceil(N / 256) is below 128 (below 256 when
+ * causal), i.e. when one workgroup per 256 query rows leaves most of the
  * GPU's 256 CUs idle (few heads and a short sequence; "Interrogating the GPU,
  * part 5", FlashAttention-2 section: batch x heads alone does not fill the
  * GPU).  A workgroup then owns 32 query
@@ -82,6 +82,25 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  */
 int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
                  int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * The forward pass through its row-block kernel (whatever the sizes) with a
+ * share of the exponentials evaluated in software on the FMA path instead of
+ * the transcendental unit ("Interrogating the GPU, part 5", section "Why did
+ * Blackwell need FlashAttention-4?": 2^x = 2^n 2^f with f in [0, 1) and 2^f
+ * from the page's cubic, relative error about 1e-4).  software_share is how
+ * many of each lane's 32 exponentials per 64-key tile take that path: 0, 8,
+ * 16 or 32 (other values: FA_ERR_INVALID_ARG, before any launch).  With 0 the
+ * results are bitwise those of the row-block kernel that fa_fwd runs for
+ * large grids.  Other arguments, outputs and error behaviour as for fa_fwd;
+ * the outputs differ from fa_fwd's by the cubic's error (LSE by about 1e-4).
+ * On this GPU the transcendental unit is not the limit (an exponential costs
+ * one instruction, the cubic ten), so fa_fwd keeps v_exp_f32; this entry
+ * point exists to measure that.
+ */
+int fa_fwd_soft_exp2(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int N, int d, float scale, int causal, int software_share,
+                     void* stream);
 
 /*
  * Bytes of device workspace the backward pass needs for these sizes:

@@ -27,8 +27,8 @@ def fa():
 
 def test_header_declares_the_boundary():
     names = declared()
-    for n in ("fa_fwd", "fa_fwd_split", "fa_bwd", "fa_bwd_workspace_size", "fa_strerror",
-              "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"):
+    for n in ("fa_fwd", "fa_fwd_split", "fa_fwd_soft_exp2", "fa_bwd", "fa_bwd_workspace_size",
+              "fa_strerror", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"):
         assert n in names
 
 
@@ -56,6 +56,13 @@ def test_workspace_size(fa):
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
 
 
+def fwd_entries(lib):
+    """The forward entry points with fa_fwd's argument list (the software-exp2
+    one at a quarter of its exponentials in software)."""
+    return (lib.fa_fwd, lib.fa_fwd_split,
+            lambda *a: lib.fa_fwd_soft_exp2(*a[:-1], 8, a[-1]))
+
+
 @pytest.mark.parametrize("args,expect", [
     # (B, H, N, d, scale, causal, misalign q) -> status
     ((1, 1, 16, 64, 0.1, 0, 0), 2),
@@ -78,13 +85,13 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
 def test_fwd_rejects_bad_arguments(fa, args, expect):
     B, H, N, d, scale, causal, mis = args
     lib = fa.load_library()
-    for entry in (lib.fa_fwd, lib.fa_fwd_split):
+    for entry in fwd_entries(lib):
         assert entry(FAKE + mis, FAKE, FAKE, FAKE, FAKE, B, H, N, d, scale, causal, None) == expect
 
 
 def test_fwd_rejects_null_pointers(fa):
     lib = fa.load_library()
-    for entry in (lib.fa_fwd, lib.fa_fwd_split):
+    for entry in fwd_entries(lib):
         for i in range(5):
             ptrs = [FAKE] * 5
             ptrs[i] = None
@@ -96,6 +103,17 @@ def test_empty_problem_is_a_no_op(fa):
     assert lib.fa_fwd(None, None, None, None, None, 0, 4, 16, 128, 0.1, 0, None) == fa.FA_OK
     assert lib.fa_fwd(None, None, None, None, None, 1, 1, 0, 128, 0.1, 1, None) == fa.FA_OK
     assert lib.fa_fwd_split(None, None, None, None, None, 1, 1, 0, 128, 0.1, 1, None) == fa.FA_OK
+    assert lib.fa_fwd_soft_exp2(None, None, None, None, None, 1, 1, 0, 128, 0.1, 1, 16, None) == fa.FA_OK
+
+
+@pytest.mark.parametrize("share", [-1, 1, 4, 7, 12, 24, 31, 33, 64])
+def test_soft_exp2_rejects_bad_shares(fa, share):
+    """Only 0, 8, 16 or 32 of the 32 exponentials per tile may go through the
+    software path; anything else is refused before any launch, also for an
+    empty problem."""
+    lib = fa.load_library()
+    assert lib.fa_fwd_soft_exp2(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 128, 0.1, 1, share, None) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_soft_exp2(None, None, None, None, None, 1, 1, 0, 128, 0.1, 1, share, None) == fa.FA_ERR_INVALID_ARG
     assert lib.fa_bwd(*([None] * 9), 1, 0, 16, 128, 0.1, 0, None, 0, None) == fa.FA_OK
 
 
