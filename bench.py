@@ -272,6 +272,26 @@ def kernel_stats(samples):
             "min": min(samples)}
 
 
+def pingpong_forward(fa, torch, q, k, v, o, lse, scale, causal, B, H, N, d, stream, warmup: int,
+                     steps: int):
+    """fa_fwd_pingpong (the forward scheduled as FlashAttention-3's ping-pong:
+    "Interrogating the GPU, part 5", FlashAttention-3 section) on the step's
+    inputs and outputs, timed like the step's kernels; not part of `value`."""
+    flops = acc.fwd_flops(B, H, N, d, causal)
+    for _ in range(max(warmup, 5)):
+        fa.fa_fwd_pingpong(q, k, v, o, lse, scale, causal, stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        fa.fa_fwd_pingpong(q, k, v, o, lse, scale, causal, stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"kernel": "fwd_pp_kernel", "ms": ms, "tflops": tf,
+            "frac_of_peak": tf / acc.MI355X_BF16_DENSE_TFLOPS}
+
+
 def soft_exp2_forward(fa, torch, q, k, v, o, lse, scale, causal, B, H, N, d, stream, warmup: int,
                       steps: int):
     """The row-block forward with 0, 8, 16 or 32 of each lane's 32 exponentials
@@ -368,6 +388,7 @@ def main():
                          "256 MB last-level cache (0: no flush; the K steps then run as one graph)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward timing")
+    ap.add_argument("--no-pingpong", action="store_true", help="skip the ping-pong forward timing")
     ap.add_argument("--no-soft-exp2", action="store_true",
                     help="skip the timing of the forward with software exponentials")
     ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
@@ -613,6 +634,12 @@ def main():
         log(f"fp8 forward: quantise {fp8['quantize_ms']:.3f} ms, attention {fp8['attn_ms']:.3f} ms "
             f"({fp8['attn_tflops']:.0f} TFLOP/s credited)")
 
+    pingpong = None
+    if not args.no_pingpong:
+        pingpong = pingpong_forward(fa, torch, q, k, v, o, lse, scale, causal, B, H, N, d, stream,
+                                    args.warmup, args.steps)
+        log(f"ping-pong forward: {pingpong['ms']:.4f} ms ({pingpong['tflops']:.0f} TFLOP/s)")
+
     soft = None
     if not args.no_soft_exp2:
         soft = soft_exp2_forward(fa, torch, q, k, v, o, lse, scale, causal, B, H, N, d, stream,
@@ -650,6 +677,7 @@ def main():
         **out_extra,
         "roofline": roof,
         "fp8_forward": fp8,
+        "fwd_pingpong": pingpong,
         "fwd_soft_exp2": soft,
         "cpu_baseline": cpu,
         "source_hash": source_hash(),

@@ -9,6 +9,7 @@ Functions mirror the C entry points:
   fa_fwd(q, k, v, o, lse, scale, causal)                       -> None
   fa_fwd_split(q, k, v, o, lse, scale, causal)                 -> None
   fa_fwd_soft_exp2(q, k, v, o, lse, scale, causal, share)      -> None
+  fa_fwd_pingpong(q, k, v, o, lse, scale, causal)              -> None
   fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale, causal, ws)   -> None
   fa_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, scale, causal) -> None
   fa_bwd_dq(q, k, v, o, dO, lse, ws, dq, scale, causal)        -> None
@@ -62,6 +63,8 @@ def load_library() -> ctypes.CDLL:
         lib.fa_fwd.restype = i
         lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         lib.fa_fwd_split.restype = i
+        lib.fa_fwd_pingpong.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+        lib.fa_fwd_pingpong.restype = i
         lib.fa_fwd_soft_exp2.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
         lib.fa_fwd_soft_exp2.restype = i
         lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
@@ -144,6 +147,10 @@ def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
 
 def fa_fwd_split(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
     _fwd_call("fa_fwd_split", q, k, v, o, lse, scale, causal, stream)
+
+
+def fa_fwd_pingpong(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
+    _fwd_call("fa_fwd_pingpong", q, k, v, o, lse, scale, causal, stream)
 
 
 def fa_fwd_soft_exp2(q, k, v, o, lse, scale: float, causal: bool, share: int, stream=None) -> None:

@@ -62,6 +62,11 @@ int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* ls
   return checked_fwd(fa::launch_fwd_split, q, k, v, o, lse, B, H, N, d, scale, causal, stream);
 }
 
+int fa_fwd_pingpong(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int N, int d, float scale, int causal, void* stream) {
+  return checked_fwd(fa::launch_fwd_pingpong, q, k, v, o, lse, B, H, N, d, scale, causal, stream);
+}
+
 int fa_fwd_soft_exp2(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                      int H, int N, int d, float scale, int causal, int software_share,
                      void* stream) {

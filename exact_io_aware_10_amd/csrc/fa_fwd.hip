@@ -304,6 +304,263 @@ void fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 }
 
 // ---------------------------------------------------------------------------
+// Ping-pong forward ("Interrogating the GPU, part 5", section "What did
+// FlashAttention-3 do with Hopper?", and "FlashAttention versions", section
+// "FlashAttention-3": one group's softmax on the vector units while the other
+// group's matrix products run).  Same tiles, numerics and results contract as
+// fwd_kernel; what differs is the schedule.  Waves w and w + 4 of the
+// workgroup share a SIMD.  Each wave alternates an MFMA phase (O^T += V^T P^T
+// of the previous tile, then S^T of this tile) with a softmax phase (mask,
+// running maximum and conditional rescale, P, row sums); waves 4..7 run one
+// phase behind waves 0..3 and a workgroup barrier ends every phase, so on
+// every SIMD one wave's MFMAs meet the other wave's exponentials.  K/V tiles
+// stream through three LDS stages (tile t - 1's V is still read while tile t
+// is used and tile t + 1 loads).
+// ---------------------------------------------------------------------------
+constexpr int PP_STAGES = 3;
+__device__ __forceinline__ int opaque_int(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+constexpr int PP_STAGE = 2 * FWD_TILE;  // K tile, then V tile
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(FWD_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_pp_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                   const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
+                   float* __restrict__ lse, int BH, int N, int nqb, float sl2, uint32_t qkeep,
+                   uint32_t qflip) {
+  __shared__ __attribute__((aligned(16))) char smem[PP_STAGES * PP_STAGE];
+  const uint32_t smem_lds = lds_addr(smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: leads, 1: one phase behind
+  const int h = lane >> 5;
+  const int col = lane & 31;
+
+  int qb, bh;
+  block_head(blockIdx.x, nqb, BH, CAUSAL, CAUSAL, &qb, &bh);
+  const int q0 = qb * FWD_BR;
+  const int q0w = q0 + wave * FWD_QW;
+  const int qrow = q0w + col;
+
+  const size_t head = (size_t)bh * (size_t)N * kD;
+  const uint32_t head_bytes = (uint32_t)N * kRowBytes;
+  const rsrc_t rq = make_rsrc(q + head, head_bytes);
+  const rsrc_t rk = make_rsrc(k + head, head_bytes);
+  const rsrc_t rv = make_rsrc(v + head, head_bytes);
+
+  bf16x8 qf[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc)
+    qf[kc] = __builtin_bit_cast(
+        bf16x8, signed_operand(buf_load16(rq, (uint32_t)qrow * kRowBytes + (2 * kc + h) * 16), qkeep, qflip));
+  // Q has arrived (in the compiler's view too) before any LDS-direct load,
+  // which the compiler does not track, is in flight.
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) asm volatile("" : : "v"(qf[kc]));
+
+  const int kend = CAUSAL ? min(N, q0 + FWD_BR) : N;
+  const int T = (kend + FWD_BC - 1) / FWD_BC;
+
+  uint32_t ld_voff[FWD_LOADS];
+#pragma unroll
+  for (int n = 0; n < FWD_LOADS; ++n) {
+    const int row = 4 * FWD_WAVES * n + 4 * wave + (lane >> 4);
+    ld_voff[n] = (uint32_t)row * kRowBytes + (((lane & 15) ^ swz(row)) << 4);
+  }
+  auto issue_tile = [&](int t) {
+    const uint32_t st = smem_lds + (uint32_t)(t % PP_STAGES) * PP_STAGE;
+    const uint32_t toff = (uint32_t)t * FWD_TILE;
+#pragma unroll
+    for (int n = 0; n < FWD_LOADS; ++n) {
+      const uint32_t dst = st + (uint32_t)(4 * FWD_WAVES * n + 4 * wave) * kRowBytes;
+      dma16(rk, dst, ld_voff[n] + toff);
+      dma16(rv, dst + FWD_TILE, ld_voff[n] + toff);
+    }
+  };
+
+  int koff[8];
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) koff[kc] = tile_off(col, 2 * kc + h);
+  int voff[4][2];
+  {
+    const int tr_s = lane & 15;
+    const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (tr_s & 3);
+    const int tr_row = 4 * h + (tr_s >> 2);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int dim = 32 * mb + tr_dim;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) voff[mb][e] = tile_off8(tr_row + 8 * e, dim >> 3, (dim >> 2) & 1);
+    }
+  }
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
+  float m = -INFINITY, l = 0.f, lr = 0.f;  // as in fwd_kernel
+  f32x16 sc[2];     // S^T of the tile whose softmax phase is next
+  bf16x8 pb[2][2];  // P^T of the tile whose P V product is next
+  // A rescale decided in a softmax phase reaches O^T at the start of the
+  // next MFMA phase, before that tile's P V product (the accumulators are
+  // touched only in MFMA phases).
+  bool rescale = false;
+  float alpha_pending = 1.f;
+
+  // MFMA phase of tile tm: O^T += V^T P^T of tile tm - 1, then S^T of tile tm.
+  // Operands are read PP_AHEAD MFMAs ahead of their use (sched_barrier keeps
+  // the compiler to that depth: hoisting every read of the phase would not
+  // fit two waves' registers).
+  constexpr int PP_AHEAD = 2;
+  auto mfma_phase = [&](int tm) {
+    if (rescale) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mb][i] *= alpha_pending;
+      rescale = false;
+    }
+    if (tm > 0) {
+      // The stage offset through a register the compiler cannot follow, so
+      // that it forms eight lane addresses per phase instead of keeping
+      // every stage's addresses live across the loop.
+      const char* vb = smem + opaque_int(((tm - 1) % PP_STAGES) * PP_STAGE) + FWD_TILE;
+      bf16x8 va[PP_AHEAD + 1];
+      auto rdv = [&](int j) {  // j = 8 st + 4 u + mb
+        const char* rb = vb + (32 * (j >> 3) + 16 * ((j >> 2) & 1)) * kRowBytes;
+        va[j % (PP_AHEAD + 1)] = join(lds_read_tr(rb + voff[j & 3][0]), lds_read_tr(rb + voff[j & 3][1]));
+      };
+#pragma unroll
+      for (int j = 0; j < PP_AHEAD; ++j) rdv(j);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (j + PP_AHEAD < 16) rdv(j + PP_AHEAD);
+        acc[j & 3] = mfma32(va[j % (PP_AHEAD + 1)], pb[j >> 3][(j >> 2) & 1], acc[j & 3]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (tm < T) {
+      const char* kb = smem + opaque_int((tm % PP_STAGES) * PP_STAGE);
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[st][i] = 0.f;
+      bf16x8 ka[PP_AHEAD + 1];
+      auto rdk = [&](int j) {  // j = 2 kc + st
+        ka[j % (PP_AHEAD + 1)] = __builtin_bit_cast(bf16x8, lds_read16(kb + (j & 1) * 32 * kRowBytes, koff[j >> 1]));
+      };
+#pragma unroll
+      for (int j = 0; j < PP_AHEAD; ++j) rdk(j);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (j + PP_AHEAD < 16) rdk(j + PP_AHEAD);
+        sc[j & 1] = mfma32(ka[j % (PP_AHEAD + 1)], qf[j >> 1], sc[j & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // Softmax phase of tile tv (the same steps as fwd_kernel's).
+  auto softmax_phase = [&](int tv) {
+    const int k0 = tv * FWD_BC;
+    const bool need_mask = (CAUSAL && (k0 + FWD_BC - 1 > q0w)) || (k0 + FWD_BC > N);
+    if (need_mask) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * st + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (key >= N || (CAUSAL && key > qrow)) sc[st][i] = -INFINITY;
+        }
+    }
+    float mx = sc[0][0];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[st][i]);
+    mx = halves_max(mx);
+    const float mcand = mx * sl2;
+    if (__builtin_amdgcn_ballot_w64(mcand > m + kTau) != 0) {
+      const float mnew = fmaxf(m, mcand);
+      const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m - mnew);
+      m = mnew;
+      l *= alpha;
+      lr *= alpha;
+      alpha_pending = alpha;
+      rescale = true;
+    }
+    const float mu = (m == -INFINITY) ? 0.f : m;
+    float rs = 0.f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(__builtin_fmaf(sc[st][i], sl2, -mu));
+        sc[st][i] = p;
+        rs += p;
+      }
+    l += rs;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int b = 8 * u;
+        pb[st][u] = pack8(sc[st][b], sc[st][b + 1], sc[st][b + 2], sc[st][b + 3], sc[st][b + 4],
+                          sc[st][b + 5], sc[st][b + 6], sc[st][b + 7]);
+        const u32x4 pw = __builtin_bit_cast(u32x4, pb[st][u]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lr = add_bf16_pair(pw[e], lr);
+      }
+  };
+
+  issue_tile(0);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
+
+  // Slot s: waves 0..3 run phase s, waves 4..7 phase s - 1; phase 2t is the
+  // MFMA phase of tile t, phase 2t + 1 its softmax phase.  Tile t + 1 is
+  // requested at the start of slot 2t and waited for at the end of slot
+  // 2t + 1; its stage last held tile t - 2, whose V was last read in slot
+  // 2t - 1 (the trailing waves' MFMA phase of tile t - 1).  Every wave runs
+  // the same 2T + 2 slots and barriers.
+  for (int s = 0; s < 2 * T + 2; ++s) {
+    if ((s & 1) == 0 && (s >> 1) + 1 < T) issue_tile((s >> 1) + 1);
+    const int ph = s - grp;
+    if (ph >= 0 && ph <= 2 * T) {
+      if ((ph & 1) == 0)
+        mfma_phase(ph >> 1);
+      else if ((ph >> 1) < T)
+        softmax_phase(ph >> 1);
+    }
+    if (s & 1)
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory");
+    else
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+  }
+
+  const float lt = halves_sum(l);
+  const float lrt = halves_sum(lr);
+  if (qrow < N) {
+    const float inv = 1.f / lrt;
+    char* orow = reinterpret_cast<char*>(o + head) + (size_t)qrow * kRowBytes;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int i = 4 * g;
+        u32x2 w = {pack_bf16(acc[mb][i] * inv, acc[mb][i + 1] * inv),
+                   pack_bf16(acc[mb][i + 2] * inv, acc[mb][i + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + (32 * mb + 8 * g + 4 * h) * 2) = w;
+      }
+    if (h == 0) lse[(size_t)bh * N + qrow] = (m + __log2f(lt)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Key-split forward, for grids too small to occupy the chip.
 // ---------------------------------------------------------------------------
 // With few (batch, head) pairs and a short sequence, one workgroup per 128
@@ -620,6 +877,24 @@ hipError_t launch_fwd_soft_exp2(const void* q, const void* k, const void* v, voi
     case 32: launch_rows_sw<32>(grid, block, stream, causal, qq, kk, vv, oo, lse, BH, N, nqb, sl2, sc); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_pingpong(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int N, float scale, int causal, hipStream_t stream) {
+  const int BH = B * H;
+  const int nqb = (N + FWD_BR - 1) / FWD_BR;
+  const signed_scale sc = split_scale(scale, kSignBitsBf16);
+  const float sl2 = sc.mag * kLog2e;
+  dim3 grid((unsigned)(nqb * BH)), block(FWD_THREADS);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  uint16_t* oo = static_cast<uint16_t*>(o);
+  if (causal)
+    hipLaunchKernelGGL(fwd_pp_kernel<true>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2, sc.keep, sc.flip);
+  else
+    hipLaunchKernelGGL(fwd_pp_kernel<false>, grid, block, 0, stream, qq, kk, vv, oo, lse, BH, N, nqb, sl2, sc.keep, sc.flip);
   return hipGetLastError();
 }
 

@@ -38,6 +38,10 @@ hipError_t launch_fwd_rows(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int N, float scale, int causal, hipStream_t stream);
 hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int H, int N, float scale, int causal, hipStream_t stream);
+// The ping-pong forward (fwd_pp_kernel): the row-block tiling with waves
+// w and w + 4 of a SIMD one phase apart.
+hipError_t launch_fwd_pingpong(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int N, float scale, int causal, hipStream_t stream);
 // The row-block kernel with `share` (0, 8, 16 or 32) of each lane's 32
 // exponentials per tile computed on the FMA path (soft_exp2).
 hipError_t launch_fwd_soft_exp2(const void* q, const void* k, const void* v, void* o, float* lse,

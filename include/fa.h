@@ -84,6 +84,23 @@ int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
+ * The forward pass scheduled as a ping-pong ("Interrogating the GPU, part 5",
+ * section "What did FlashAttention-3 do with Hopper?"; "FlashAttention
+ * versions", section "FlashAttention-3": one group's softmax runs on the
+ * vector units while the other group's matrix products run).  The row-block
+ * tiling of fa_fwd (256 query rows per workgroup, 64-key tiles, eight
+ * wavefronts, two per SIMD), with waves w and w + 4 of a SIMD alternating an
+ * MFMA phase and a softmax phase one phase apart, so that one's matrix
+ * products meet the other's exponentials.  Same arithmetic as fa_fwd's
+ * row-block kernel (results equal to rounding order, not bitwise);
+ * arguments, outputs and error behaviour as for fa_fwd.  Exported to measure
+ * that schedule against fa_fwd's, whose two waves per SIMD interleave by
+ * themselves.
+ */
+int fa_fwd_pingpong(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
  * The forward pass through its row-block kernel (whatever the sizes) with a
  * share of the exponentials evaluated in software on the FMA path instead of
  * the transcendental unit ("Interrogating the GPU, part 5", section "Why did

@@ -27,7 +27,7 @@ def fa():
 
 def test_header_declares_the_boundary():
     names = declared()
-    for n in ("fa_fwd", "fa_fwd_split", "fa_fwd_soft_exp2", "fa_bwd", "fa_bwd_workspace_size",
+    for n in ("fa_fwd", "fa_fwd_split", "fa_fwd_soft_exp2", "fa_fwd_pingpong", "fa_bwd", "fa_bwd_workspace_size",
               "fa_strerror", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"):
         assert n in names
 
@@ -59,7 +59,7 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
 def fwd_entries(lib):
     """The forward entry points with fa_fwd's argument list (the software-exp2
     one at a quarter of its exponentials in software)."""
-    return (lib.fa_fwd, lib.fa_fwd_split,
+    return (lib.fa_fwd, lib.fa_fwd_split, lib.fa_fwd_pingpong,
             lambda *a: lib.fa_fwd_soft_exp2(*a[:-1], 8, a[-1]))
 
 
@@ -104,6 +104,7 @@ def test_empty_problem_is_a_no_op(fa):
     assert lib.fa_fwd(None, None, None, None, None, 1, 1, 0, 128, 0.1, 1, None) == fa.FA_OK
     assert lib.fa_fwd_split(None, None, None, None, None, 1, 1, 0, 128, 0.1, 1, None) == fa.FA_OK
     assert lib.fa_fwd_soft_exp2(None, None, None, None, None, 1, 1, 0, 128, 0.1, 1, 16, None) == fa.FA_OK
+    assert lib.fa_fwd_pingpong(None, None, None, None, None, 1, 1, 0, 128, 0.1, 1, None) == fa.FA_OK
 
 
 @pytest.mark.parametrize("share", [-1, 1, 4, 7, 12, 24, 31, 33, 64])
