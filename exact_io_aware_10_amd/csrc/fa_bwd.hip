@@ -508,11 +508,15 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 // operands of S^T = K Q^T and dP^T = V dO^T) loaded once, Q into AGPRs, and
 // the dQ^T accumulators (128 registers) in AGPRs as well.  32-key tiles of K and V
 // stream through a five-slot LDS ring.  Owning 64 queries lets every K or V
-// fragment read from LDS feed two MFMAs.  Per tile t and wave:
+// fragment read from LDS feed two MFMAs.  Before the loop the kernel also
+// loads O beside dO and forms -D = -rowsum(dO o O) and L log2(e) of its
+// queries, which its dP chains start from and which it writes to the
+// workspace for the dK/dV kernel (no pre-pass launch).  Per tile t and wave:
 //   A  S^T  = K_t Q^T      16 MFMAs (VGPR accumulators, inline assembly)
 //   B  dP^T - D = V_t dO^T - D   16 MFMAs (the chain starts from -D of the
 //                          lane's query), interleaved with P = exp2(S scale
 //                          log2 e - L log2 e) of tile t
+//   the ring barrier for tile t + 1, and that tile's first K reads
 //   C  dQ^T += K_{t-1}^T dS_{t-1}^T   16 MFMAs, interleaved with
 //                          dS = P (dP - D) of tile t (one multiply), packed to bf16
 // ---------------------------------------------------------------------------
