@@ -57,11 +57,38 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without its comments (// to end of line, /* ... */), string
+    literals kept as they are."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c == '"':
+            j = i + 1
+            while j < n and src[j] != '"':
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def source_hash() -> str:
+    """Hash of the kernel and boundary sources with comments removed and
+    whitespace collapsed: the counters in profiles/traffic.json stay valid
+    across edits of comments and layout."""
     h = hashlib.sha256()
     for f in KERNEL_FILES:
-        with open(os.path.join(ROOT, "exact_io_aware_10_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "exact_io_aware_10_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(" ".join(strip_comments(fh.read()).split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -50,3 +50,14 @@ def test_power_sampler_reads_a_sysfs_tree(tmp_path):
     assert got["power_cap_w"] == 1400.0
     assert got["sclk_mhz_mean"] == got["sclk_mhz_min"] == 1882.0
     assert none is None
+
+
+def test_source_hash_ignores_comments_and_layout():
+    """The hash that ties profiles/traffic.json to the kernel sources changes
+    with the code, not with comments or whitespace; comment markers inside
+    string literals (inline assembly) are code."""
+    import bench
+    src = 'int a = 1; // one\n/* block\n comment */ asm("s_nop 1 // not a comment");\n'
+    assert bench.strip_comments(src).split() == ['int', 'a', '=', '1;', 'asm("s_nop', '1', '//', 'not', 'a', 'comment");']
+    assert " ".join(bench.strip_comments("x /* a */ + y // b\n").split()) == "x + y"
+    assert len(bench.source_hash()) == 16
