@@ -59,11 +59,13 @@ def _max_dev_err(torch, got, want_pool):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_forward_both_kernels_at_the_largest_size(fa, pool, causal):
+def test_forward_every_kernel_at_the_largest_size(fa, pool, causal):
     import torch
     q, k, v = (_tile(torch, pool[n]) for n in "qkv")
     ro, rl = ora.forward(f64(pool["q"]), f64(pool["k"]), f64(pool["v"]), fa_inputs.SCALE, causal)
-    for name, entry in (("fa_fwd", fa.fa_fwd), ("fa_fwd_split", fa.fa_fwd_split)):
+    soft16 = lambda *a: fa.fa_fwd_soft_exp2(*a, 16)  # noqa: E731  (half the exponentials in software)
+    for name, entry in (("fa_fwd", fa.fa_fwd), ("fa_fwd_split", fa.fa_fwd_split),
+                        ("fa_fwd_pingpong", fa.fa_fwd_pingpong), ("fa_fwd_soft_exp2", soft16)):
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
         entry(q, k, v, o, lse, fa_inputs.SCALE, causal)
