@@ -50,7 +50,7 @@ import fa_inputs  # noqa: E402
 from exact_io_aware_10_amd import accounting as acc  # noqa: E402
 
 METRIC = "attention fwd/bwd TFLOP/s at d=128 bf16, % of MI355X dense bf16 MFMA peak"
-KERNEL_FILES = ("fa_device.hpp", "fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip", "fa_api.cpp", "fa_internal.h")
+KERNEL_FILES = ("fa_device.hpp", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_atomic.hip", "fa_fp8.hip", "fa_api.cpp", "fa_internal.h")
 
 
 def log(*a):
@@ -299,6 +299,30 @@ def kernel_stats(samples):
             "min": min(samples)}
 
 
+def atomic_dq_backward(fa, torch, q, k, v, o, do, lse, scale, causal, B, H, N, d, stream,
+                       warmup: int, steps: int):
+    """fa_bwd_atomic_dq (dQ fused into the dK/dV pass through fp32 atomics; "LLM
+    flash attention", section "End-to-end flow") on the step's inputs: its four
+    launches timed together with HIP events on the launch stream, credited the
+    backward's FLOPs; not part of `value`."""
+    flops = acc.bwd_flops(B, H, N, d, causal)
+    ws = torch.empty(fa.fa_bwd_atomic_workspace_size(B, H, N, d, causal), dtype=torch.uint8, device=q.device)
+    g = [torch.empty_like(q) for _ in range(3)]
+    for _ in range(max(warmup, 5)):
+        fa.fa_bwd_atomic_dq(q, k, v, o, do, lse, *g, scale, causal, ws, stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        fa.fa_bwd_atomic_dq(q, k, v, o, do, lse, *g, scale, causal, ws, stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    tf = flops / (ms * 1e-3) / 1e12
+    del ws, g
+    return {"kernels": "bwd_pre_kernel, dq_clear_kernel, bwd_atomic_kernel, dq_convert_kernel", "ms": ms,
+            "tflops": tf, "frac_of_peak": tf / acc.MI355X_BF16_DENSE_TFLOPS}
+
+
 def pingpong_forward(fa, torch, q, k, v, o, lse, scale, causal, B, H, N, d, stream, warmup: int,
                      steps: int):
     """fa_fwd_pingpong (the forward scheduled as FlashAttention-3's ping-pong:
@@ -416,6 +440,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward timing")
     ap.add_argument("--no-pingpong", action="store_true", help="skip the ping-pong forward timing")
+    ap.add_argument("--no-atomic-dq", action="store_true",
+                    help="skip the timing of the backward with dQ fused through atomics")
     ap.add_argument("--no-soft-exp2", action="store_true",
                     help="skip the timing of the forward with software exponentials")
     ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
@@ -667,6 +693,12 @@ def main():
                                     args.warmup, args.steps)
         log(f"ping-pong forward: {pingpong['ms']:.4f} ms ({pingpong['tflops']:.0f} TFLOP/s)")
 
+    atomic = None
+    if with_bwd and not args.no_atomic_dq:
+        atomic = atomic_dq_backward(fa, torch, q, k, v, o, do, lse, scale, causal, B, H, N, d, stream,
+                                    args.warmup, args.steps)
+        log(f"backward with fused atomic dQ: {atomic['ms']:.4f} ms ({atomic['tflops']:.0f} TFLOP/s)")
+
     soft = None
     if not args.no_soft_exp2:
         soft = soft_exp2_forward(fa, torch, q, k, v, o, lse, scale, causal, B, H, N, d, stream,
@@ -705,6 +737,7 @@ def main():
         "roofline": roof,
         "fp8_forward": fp8,
         "fwd_pingpong": pingpong,
+        "bwd_atomic_dq": atomic,
         "fwd_soft_exp2": soft,
         "cpu_baseline": cpu,
         "source_hash": source_hash(),

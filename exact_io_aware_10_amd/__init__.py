@@ -12,6 +12,8 @@ Functions mirror the C entry points:
   fa_fwd_pingpong(q, k, v, o, lse, scale, causal)              -> None
   fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale, causal, ws)   -> None
   fa_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, scale, causal) -> None
+  fa_bwd_atomic_dq(q, k, v, o, dO, lse, dq, dk, dv, scale, causal, ws) -> None
+  fa_bwd_atomic_workspace_size(B, H, N, d, causal)             -> int
   fa_bwd_dq(q, k, v, o, dO, lse, ws, dq, scale, causal)        -> None
   fa_bwd_dkdv(q, k, v, dO, ws, dk, dv, scale, causal)          -> None
   fa_bwd_preprocess(o, dO, lse, ws)                            -> None
@@ -73,6 +75,10 @@ def load_library() -> ctypes.CDLL:
         lib.fa_bwd.restype = i
         lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
         lib.fa_bwd_noalloc.restype = i
+        lib.fa_bwd_atomic_workspace_size.argtypes = [i, i, i, i, i]
+        lib.fa_bwd_atomic_workspace_size.restype = sz
+        lib.fa_bwd_atomic_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, sz, vp]
+        lib.fa_bwd_atomic_dq.restype = i
         lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, vp]
         lib.fa_bwd_preprocess.restype = i
         lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, f, i, vp]
@@ -99,6 +105,11 @@ def fa_strerror(status: int) -> str:
 
 def fa_bwd_workspace_size(B: int, H: int, N: int, d: int = HEAD_DIM, causal: bool = False) -> int:
     return int(load_library().fa_bwd_workspace_size(B, H, N, d, int(bool(causal))))
+
+
+def fa_bwd_atomic_workspace_size(B: int, H: int, N: int, d: int = HEAD_DIM,
+                                 causal: bool = False) -> int:
+    return int(load_library().fa_bwd_atomic_workspace_size(B, H, N, d, int(bool(causal))))
 
 
 def _ptr(t):
@@ -177,6 +188,23 @@ def fa_bwd(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, workspac
     st = load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
                                _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
                                _ptr(workspace), nbytes, _stream(stream))
+    if st != FA_OK:
+        raise FAError(st)
+
+
+def fa_bwd_atomic_dq(q, k, v, o, do, lse, dq, dk, dv, scale: float, causal: bool, workspace,
+                     stream=None) -> None:
+    B, H, N, d = _shape(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dO", do), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        _check_tensor(name, t, torch.bfloat16, (B, H, N, d))
+    _check_tensor("lse", lse, torch.float32, (B, H, N))
+    if workspace.device.type != "cuda" or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load_library().fa_bwd_atomic_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                         _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
+                                         int(bool(causal)), _ptr(workspace), nbytes, _stream(stream))
     if st != FA_OK:
         raise FAError(st)
 

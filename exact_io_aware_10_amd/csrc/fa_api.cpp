@@ -178,6 +178,31 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_bwd_atomic_workspace_size(int B, int H, int N, int d, int causal) {
+  bool empty = false;
+  if (check_common(B, H, N, d, 1.f, causal, &empty) != FA_OK) return 0;
+  if (empty) return 0;
+  return fa::bwd_atomic_dq_offset(B, H, N) + (size_t)B * H * N * d * sizeof(float);
+}
+
+int fa_bwd_atomic_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                     float scale, int causal, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, causal, &empty);
+  if (st != FA_OK || empty) return st;
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_bwd_atomic_workspace_size(B, H, N, d, causal);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  hipError_t e = fa::launch_bwd_atomic(q, k, v, o, dO, lse, workspace, dq, dk, dv, B, H, N, scale,
+                                       causal, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_fp8_codes_size(int B, int H, int N, int d, int layout) {
   bool empty = false;
   if (check_common(B, H, N, d, 1.f, 0, &empty) != FA_OK || empty) return 0;

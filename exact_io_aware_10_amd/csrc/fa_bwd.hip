@@ -32,11 +32,6 @@
 
 namespace fa {
 
-__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
-}
-
-
 // MFMA with the accumulator in VGPRs, as inline assembly.  In kernels that
 // run one wave per SIMD the compiler gives every MFMA an AGPR accumulator;
 // the score tiles S and dP are read by VALU code right after, so they are

@@ -131,6 +131,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
 // 16 bytes per lane from global memory straight into LDS: lane i writes
 // lds_base + 16 i (lds_base must be wave-uniform).  The global byte offset
 // voff is per lane and is the part the hardware range-checks.

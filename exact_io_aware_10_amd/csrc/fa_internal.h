@@ -48,6 +48,14 @@ hipError_t launch_fwd_soft_exp2(const void* q, const void* k, const void* v, voi
                                 int B, int H, int N, float scale, int causal, int share,
                                 hipStream_t stream);
 
+// Fused backward with atomic dQ: workspace [-D | L log2(e)] (padded to 256
+// bytes, bwd_atomic_dq_offset) followed by an fp32 dQ buffer of B*H*N*128.
+size_t bwd_atomic_dq_offset(int B, int H, int N);
+hipError_t launch_bwd_atomic(const void* q, const void* k, const void* v, const void* o,
+                             const void* dO, const float* lse, void* ws, void* dq, void* dk,
+                             void* dv, int B, int H, int N, float scale, int causal,
+                             hipStream_t stream);
+
 // Backward workspace layout (2 B*H*N floats): [-D = -rowsum(dO * O) | L * log2(e)].
 hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* ws, int B, int H,
                           int N, hipStream_t stream);

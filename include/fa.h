@@ -167,6 +167,33 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                    int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
+ * Workspace bytes for fa_bwd_atomic_dq: the [-D | L*log2(e)] workspace of
+ * fa_bwd padded to 256 bytes, then an fp32 dQ buffer of B*H*N*d floats.
+ * Returns 0 when the sizes are invalid or empty.
+ */
+size_t fa_bwd_atomic_workspace_size(int B, int H, int N, int d, int causal);
+
+/*
+ * The backward pass with dQ fused into the dK/dV pass through fp32 atomics
+ * ("LLM flash attention", section "End-to-end flow": each key block adds its
+ * share of dQ_i = sum_j dS_ij K_j).  Four launches: the pre-pass (-D and
+ * L*log2(e)), a clear of the fp32 dQ buffer, the fused kernel (128 keys per
+ * workgroup: dK, dV, and dS K summed over the workgroup in LDS, then one
+ * fp32 global atomic add per element and 32-query tile), and a conversion
+ * of the buffer to bf16 dQ times the scale.  Same arguments, outputs and
+ * tolerances as fa_bwd, with the workspace sized by
+ * fa_bwd_atomic_workspace_size (its contents on entry are ignored); dK and
+ * dV are deterministic, dQ is not bitwise reproducible (the order of the
+ * atomic additions varies).  On this GPU it is slower than fa_bwd: the
+ * atomic traffic alone outweighs the dQ kernel's two recomputed products,
+ * which is why fa_bwd keeps the separate dQ kernel; exported to measure that.
+ */
+int fa_bwd_atomic_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv,
+                     int B, int H, int N, int d, float scale, int causal,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The stages of the backward, each exposed so that a caller can schedule or
  * time them separately.  fa_bwd runs fa_bwd_dq, then fa_bwd_dkdv, on one
  * stream; running those two with the same arguments and workspace is exactly

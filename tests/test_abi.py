@@ -27,7 +27,8 @@ def fa():
 
 def test_header_declares_the_boundary():
     names = declared()
-    for n in ("fa_fwd", "fa_fwd_split", "fa_fwd_soft_exp2", "fa_fwd_pingpong", "fa_bwd", "fa_bwd_workspace_size",
+    for n in ("fa_fwd", "fa_fwd_split", "fa_fwd_soft_exp2", "fa_fwd_pingpong", "fa_bwd_atomic_dq",
+              "fa_bwd_atomic_workspace_size", "fa_bwd", "fa_bwd_workspace_size",
               "fa_strerror", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq"):
         assert n in names
 
@@ -116,6 +117,22 @@ def test_soft_exp2_rejects_bad_shares(fa, share):
     assert lib.fa_fwd_soft_exp2(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 16, 128, 0.1, 1, share, None) == fa.FA_ERR_INVALID_ARG
     assert lib.fa_fwd_soft_exp2(None, None, None, None, None, 1, 1, 0, 128, 0.1, 1, share, None) == fa.FA_ERR_INVALID_ARG
     assert lib.fa_bwd(*([None] * 9), 1, 0, 16, 128, 0.1, 0, None, 0, None) == fa.FA_OK
+
+
+def test_atomic_dq_workspace(fa):
+    """fa_bwd_atomic_dq needs the [-D | L log2 e] workspace (padded to 256
+    bytes) plus an fp32 dQ buffer, and refuses anything smaller before any
+    launch."""
+    lib = fa.load_library()
+    n = lib.fa_bwd_atomic_workspace_size(1, 2, 100, 128, 1)
+    assert n == 1792 + 1 * 2 * 100 * 128 * 4  # 2*200 floats = 1600 bytes, padded to 1792
+    assert lib.fa_bwd_atomic_workspace_size(1, 2, 0, 128, 1) == 0
+    assert lib.fa_bwd_atomic_workspace_size(1, 2, 100, 64, 1) == 0
+    p = [FAKE] * 9
+    assert lib.fa_bwd_atomic_dq(*p, 1, 2, 100, 128, 0.1, 1, FAKE, n - 16, None) == fa.FA_ERR_WORKSPACE
+    assert lib.fa_bwd_atomic_dq(*p, 1, 2, 100, 128, 0.1, 1, None, n, None) == fa.FA_ERR_WORKSPACE
+    assert lib.fa_bwd_atomic_dq(*([None] * 9), 1, 2, 0, 128, 0.1, 1, None, 0, None) == fa.FA_OK
+    assert lib.fa_bwd_atomic_dq(*([None] * 9), 1, 2, 16, 128, 0.1, 1, FAKE, n, None) == fa.FA_ERR_INVALID_ARG
 
 
 def test_bwd_rejects_bad_workspace(fa):
