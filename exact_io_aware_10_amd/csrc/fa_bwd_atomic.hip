@@ -12,7 +12,7 @@
 // query-major order, K^T read transposed from the LDS K block), the four
 // waves' partials stored to LDS and summed, and the sum added to an fp32 dQ
 // buffer with one global atomic per element and tile.  A second kernel turns
-// that buffer into bf16 dQ (times the signed scale).  The forward pre-pass
+// that buffer into bf16 dQ (times the signed scale).  The backward pre-pass
 // (bwd_pre_kernel) supplies -D and L log2 e.
 //
 // The dQ summation order across key blocks is whatever order the atomics land
