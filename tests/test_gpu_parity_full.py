@@ -149,10 +149,17 @@ def test_fwd_causal_b1_h8_n32768_std4(fa):
                worst)
 
 
-def _backward_every_head(fa, name):
+def _backward_every_head(fa, name, shape=None):
+    """O, LSE, dQ, dK, dV of every head against the oracle: a named workload,
+    or `shape` = (B, H, N, causal, seed) for another size."""
     import torch
-    w = fa_inputs.WORKLOADS[name]
-    x = fa_inputs.make_workload(name, with_do=True)
+    if shape is None:
+        w = fa_inputs.WORKLOADS[name]
+        x = fa_inputs.make_workload(name, with_do=True)
+    else:
+        B, H, N, causal, seed = shape
+        w = {"B": B, "H": H, "N": N, "causal": causal}
+        x = fa_inputs.make(B, H, N, seed=seed, with_do=True)
     q, k, v, do = (to_dev(x[n], torch) for n in ("q", "k", "v", "do"))
     o, lse = fa.forward(q, k, v, fa_inputs.SCALE, w["causal"])
     dq, dk, dv = fa.backward(q, k, v, o, do, lse, fa_inputs.SCALE, w["causal"])
@@ -183,6 +190,13 @@ def _backward_every_head(fa, name):
 @pytest.mark.timeout(900)
 def test_fwd_bwd_causal_b2_h16_n4096_every_head(fa):
     _backward_every_head(fa, "causal_b2_h16_n4096")
+
+
+@pytest.mark.timeout(900)
+def test_fwd_bwd_non_causal_b1_h8_n4096_every_head(fa):
+    """The non-causal gradient kernels (their own instantiations, every tile
+    unmasked but the tail) at a multi-tile size: every head."""
+    _backward_every_head(fa, "non-causal B1 H8 N4096", shape=(1, 8, 4096, False, 9500))
 
 
 @pytest.mark.timeout(1200)
