@@ -681,30 +681,46 @@ def main():
     roof["work"] = what
     roof["avg_launch_ms"] = kern_ms[dom]
 
+    # The extra legs run after the timed step and do not enter `value`; an
+    # exception in one (an allocation, a status code) is recorded in its field
+    # instead of ending the run.
+    def leg(name, fn, summary):
+        try:
+            r = fn()
+        except Exception as e:  # noqa: BLE001  (any failure of an auxiliary leg)
+            log(f"{name}: failed ({type(e).__name__}: {e})")
+            return {"error": f"{type(e).__name__}: {e}"}
+        log(summary(r))
+        return r
+
     fp8 = None
     if not args.no_fp8:
-        fp8 = fp8_forward(fa, torch, q, k, v, w, args.workload, stream, args.warmup, args.steps)
-        log(f"fp8 forward: quantise {fp8['quantize_ms']:.3f} ms, attention {fp8['attn_ms']:.3f} ms "
-            f"({fp8['attn_tflops']:.0f} TFLOP/s credited)")
+        fp8 = leg("fp8 forward",
+                  lambda: fp8_forward(fa, torch, q, k, v, w, args.workload, stream, args.warmup, args.steps),
+                  lambda r: f"fp8 forward: quantise {r['quantize_ms']:.3f} ms, attention {r['attn_ms']:.3f} ms "
+                            f"({r['attn_tflops']:.0f} TFLOP/s credited)")
 
     pingpong = None
     if not args.no_pingpong:
-        pingpong = pingpong_forward(fa, torch, q, k, v, o, lse, scale, causal, B, H, N, d, stream,
-                                    args.warmup, args.steps)
-        log(f"ping-pong forward: {pingpong['ms']:.4f} ms ({pingpong['tflops']:.0f} TFLOP/s)")
+        pingpong = leg("ping-pong forward",
+                       lambda: pingpong_forward(fa, torch, q, k, v, o, lse, scale, causal, B, H, N, d,
+                                                stream, args.warmup, args.steps),
+                       lambda r: f"ping-pong forward: {r['ms']:.4f} ms ({r['tflops']:.0f} TFLOP/s)")
 
     atomic = None
     if with_bwd and not args.no_atomic_dq:
-        atomic = atomic_dq_backward(fa, torch, q, k, v, o, do, lse, scale, causal, B, H, N, d, stream,
-                                    args.warmup, args.steps)
-        log(f"backward with fused atomic dQ: {atomic['ms']:.4f} ms ({atomic['tflops']:.0f} TFLOP/s)")
+        atomic = leg("backward with fused atomic dQ",
+                     lambda: atomic_dq_backward(fa, torch, q, k, v, o, do, lse, scale, causal, B, H, N, d,
+                                                stream, args.warmup, args.steps),
+                     lambda r: f"backward with fused atomic dQ: {r['ms']:.4f} ms ({r['tflops']:.0f} TFLOP/s)")
 
     soft = None
     if not args.no_soft_exp2:
-        soft = soft_exp2_forward(fa, torch, q, k, v, o, lse, scale, causal, B, H, N, d, stream,
-                                 args.warmup, args.steps)
-        log("forward with software exponentials (share of 32 per tile: ms): "
-            + ", ".join(f"{s_}: {r['ms']:.4f}" for s_, r in soft["by_share"].items()))
+        soft = leg("forward with software exponentials",
+                   lambda: soft_exp2_forward(fa, torch, q, k, v, o, lse, scale, causal, B, H, N, d, stream,
+                                             args.warmup, args.steps),
+                   lambda r: "forward with software exponentials (share of 32 per tile: ms): "
+                             + ", ".join(f"{s_}: {x_['ms']:.4f}" for s_, x_ in r["by_share"].items()))
 
     cpu = None
     if not args.no_cpu_baseline:
